@@ -1,0 +1,39 @@
+"""Flop accounting (host logic) pinned to the counts printed on the pages."""
+import json
+import os
+
+from newton_schulz_matrix_muon_amd import flops
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+C = json.load(open(os.path.join(HERE, "golden", "pages_constants.json")))
+
+
+def test_dense_standard_count_is_the_articles_three_products():
+    # 2 m n^2 (X X^T) + 2 n^3 (A^2) + 2 m n^2 (B X) per iteration, X in R^{n x m}
+    assert set(C["standard_ns_flops_per_iteration"]["terms"]) == {"XXT", "A2", "BX"}
+    for n, m in [(128, 512), (1408, 2048), (2048, 7168), (7168, 18432)]:
+        per_it = 2 * m * n ** 2 + 2 * n ** 3 + 2 * m * n ** 2
+        assert flops.standard_dense_flops(n, m, 1) == per_it
+        assert flops.standard_dense_flops(m, n, 5) == 5 * per_it     # orientation
+
+
+def test_gram_product_counts():
+    assert flops.gram_products(5, ()) == (17, 1, 1)
+    assert flops.gram_products(5, (2,)) == (14, 2, 2)
+
+
+def test_reduction_range_against_the_article():
+    lo, hi = C["gram_flop_reduction_range"]["low"], C["gram_flop_reduction_range"]["high"]
+    red = []
+    for n, m in [(1408, 2048), (2048, 4096), (2048, 7168), (128, 512)]:
+        red.append(1 - flops.gram_flops(n, m) / flops.standard_dense_flops(n, m))
+    assert all(lo - 0.005 <= r <= hi + 0.005 for r in red), red
+    assert abs(red[0] - 0.418) < 0.002 and abs(red[-1] - 0.576) < 0.002
+
+
+def test_workload_totals():
+    k2 = C["kimi_k2_ns_workload"]
+    n, m = k2["expert_shape"]
+    assert abs(flops.standard_flops(n, m) / 1e9 - 494.0) < 0.1
+    assert abs(flops.gram_flops(n, m, restarts=()) / 1e9 - 236.3) < 0.1
+    assert abs(flops.gram_flops(n, m) / 1e9 - 300.7) < 0.1
