@@ -1,0 +1,225 @@
+"""Throughput of the Muon hot path on one MI355X, as one JSON line.
+
+A step is one fused Muon step (momentum -> Frobenius norm -> Newton-Schulz -> update scale ->
+decoupled weight decay) over the whole synthetic batch, through the C ABI. The default
+workload is the Kimi-K2-shaped expert batch: 648 bf16 matrices of 2048 x 7168 (216 experts x
+up/gate/down), Gaussian entries plus a rank-32 spike, with stabilized Gram Newton-Schulz
+(fp16 iterates, restart after step 2, K = 5). The standard iteration is timed beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant gram|standard]
+                    [--batch B] [--no-cpu-baseline] [--skip-standard]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kind_work(kind: str, B: int, n: int, m: int):
+    """Algorithmic work of one launch of a kernel kind: (amount, unit, bound)."""
+    from newton_schulz_matrix_muon_amd import flops
+    if kind == "gemm_symprod":
+        return B * flops.sym_flops(n, n), "flop", "mfma"
+    if kind == "gemm_syrk":
+        return B * flops.sym_flops(n, m), "flop", "mfma"
+    if kind == "gemm_rect":
+        return B * flops.rect_flops(n, m), "flop", "mfma"
+    if kind == "prep_norm":
+        # read G (bf16) and M (fp32), write M (fp32) and the two bf16 copies of N
+        return B * n * m * (2 + 4 + 4 + 2 + 2), "byte", "hbm"
+    return None
+
+
+def cpu_baseline(G_host, W_host, budget_s: float, variant: str):
+    """The fp64 oracle's Muon step on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    ns = (lambda x: oracle.ns_gram(x, restarts=(2,))) if variant == "gram" else oracle.ns_standard
+    done, t0 = 0, time.perf_counter()
+    while done < len(G_host):
+        oracle.muon_step(W_host[done], G_host[done], np.zeros_like(G_host[done]), 0.02, 0.95,
+                         0.01, nesterov=True, ns=ns)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of the batch's matrices, fused Muon step with "
+                      f"{'stabilized Gram' if variant == 'gram' else 'standard'} Newton-Schulz, "
+                      f"numpy fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--variant", choices=["gram", "standard"], default="gram")
+    ap.add_argument("--batch", type=int, default=648)
+    ap.add_argument("--rows", type=int, default=2048)
+    ap.add_argument("--cols", type=int, default=7168)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-standard", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the batch dimension would shard "
+                          "across GPUs (see DESIGN.md), but --gpus > 1 is not supported"}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    from newton_schulz_matrix_muon_amd import flops, ops
+
+    dev = torch.device("cuda:0")
+    B, r, c = args.batch, args.rows, args.cols
+    n, m = min(r, c), max(r, c)
+    log(f"generating {B} x {r} x {c} bf16 gradients (Gaussian + rank-32 spike)")
+    G = synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device=dev)
+    W = synth.torch_weights(B, r, c, workload_index=2, device=dev)
+    M = torch.zeros(B, r, c, dtype=torch.float32, device=dev)
+    steps_kw = dict(lr=0.02, momentum=0.95, weight_decay=0.01, scale_coeff=0.2, nesterov=True)
+
+    p_g = ops.ns_params(io_dtype=ops.BF16, restart_mask=1 << 2)
+    p_s = ops.ns_params(io_dtype=ops.BF16, restart_mask=0)
+    ws_bytes = max(ops.workspace_bytes(ops.GRAM, G, p_g), ops.workspace_bytes(ops.STANDARD, G, p_s))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    log(f"workspace {ws_bytes / 1e9:.1f} GB")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        k = 4
+        Gh = G[:k].double().cpu().numpy()
+        Wh = W[:k].double().cpu().numpy()
+
+    def step(variant_code):
+        ops.muon_step(W, G, M, variant=variant_code, workspace=ws, **steps_kw)
+
+    def timed(variant_code, steps, warmup, with_kernel_timing):
+        for _ in range(warmup):
+            step(variant_code)
+        torch.cuda.synchronize()
+        if with_kernel_timing:
+            ops.timing_reset()
+            ops.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(variant_code)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        kt = None
+        if with_kernel_timing:
+            ops.timing_enable(False)
+            kt = ops.timing_query()
+        return dt / steps, kt
+
+    main_code = ops.GRAM if args.variant == "gram" else ops.STANDARD
+    log(f"timing {args.variant}: warmup {args.warmup}, steps {args.steps}")
+    sec, kt = timed(main_code, args.steps, args.warmup, True)
+    # event timing adds a few microseconds per launch; report the untimed run too
+    sec_plain, _ = timed(main_code, max(1, args.steps // 2), 0, False)
+    log(f"{args.variant}: {sec * 1e3:.2f} ms/step (with events), {sec_plain * 1e3:.2f} ms/step plain")
+
+    def algo(variant):
+        return flops.gram_flops(r, c) if variant == "gram" else flops.standard_flops(r, c)
+
+    variants = {}
+    def summarize(name, s):
+        f = B * algo(name)
+        variants[name] = {"ms_per_step": s * 1e3, "matrices_per_s": B / s,
+                          "executed_tflops": f / s / 1e12,
+                          "frac_bf16_peak": f / s / 1e12 / PEAK_MFMA_TFLOPS,
+                          "std_equivalent_tflops": B * flops.standard_dense_flops(r, c) / s / 1e12}
+    summarize(args.variant, sec)
+    if not args.skip_standard:
+        other = "standard" if args.variant == "gram" else "gram"
+        oc = ops.STANDARD if other == "standard" else ops.GRAM
+        log(f"timing {other}")
+        s2, _ = timed(oc, max(1, args.steps // 2), 1, False)
+        summarize(other, s2)
+        log(f"{other}: {s2 * 1e3:.2f} ms/step")
+
+    # dominant kernel and its roofline
+    kinds = {k: v for k, v in kt.items() if v[1] > 0}
+    dom = max(kinds, key=lambda k: kinds[k][0])
+    tot_ms, launches = kinds[dom]
+    avg_s = tot_ms / launches / 1e3
+    amount, unit, bound = kind_work(dom, B, n, m)
+    if unit == "flop":
+        achieved = amount / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None}
+    else:
+        achieved = amount / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = avg_s * 1e3
+    roof["launches"] = launches
+    per_kind = {}
+    for k, (ms, cnt) in kinds.items():
+        w = kind_work(k, B, n, m)
+        e = {"total_ms_per_step": ms / args.steps, "launches_per_step": cnt / args.steps,
+             "avg_launch_ms": ms / cnt}
+        if w:
+            amt, u, _ = w
+            e["achieved"] = amt / (ms / cnt / 1e3) / (1e12 if u == "flop" else 1e9)
+            e["unit"] = "TFLOP/s" if u == "flop" else "GB/s"
+        per_kind[k] = e
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(Gh, Wh, args.cpu_budget, args.variant)
+
+    out = {
+        "metric": "NS-orthogonalized matrices/sec and effective TFLOP/s (% bf16 MFMA peak)",
+        "value": B / sec,
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"kimi_k2_experts_{B}x{r}x{c}_bf16_gaussian_plus_rank32_spike",
+                   "batch": B, "rows": r, "cols": c,
+                   "step": f"fused Muon step, {args.variant} Newton-Schulz K=5"
+                           + (" (fp16 iterates, restart after step 2)" if args.variant == "gram" else ""),
+                   "lr": 0.02, "momentum": 0.95, "nesterov": True, "weight_decay": 0.01,
+                   "scale": "0.2*sqrt(max(rows, cols))"},
+        "effective_tflops": variants[args.variant]["executed_tflops"],
+        "frac_bf16_peak": variants[args.variant]["frac_bf16_peak"],
+        "ms_per_step_plain": sec_plain * 1e3,
+        "variants": variants,
+        "kernels": per_kind,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

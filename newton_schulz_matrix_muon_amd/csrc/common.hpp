@@ -1,0 +1,65 @@
+// Shared device helpers for the gfx950 kernels: element types, loads/stores by runtime
+// dtype, and the XCD-aware workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mns {
+
+enum Dtype : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int dtype_size(int dt) { return dt == F32 ? 4 : 2; }
+
+// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
+__device__ inline uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ inline uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // hardware conversion, round-to-nearest-even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Load element `idx` of a buffer of runtime dtype `dt` as fp32.
+__device__ inline float load_elem(const void* p, int dt, int64_t idx) {
+  if (dt == F32) return reinterpret_cast<const float*>(p)[idx];
+  uint16_t h = reinterpret_cast<const uint16_t*>(p)[idx];
+  return dt == BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+// Store fp32 `v` into element `idx` of a buffer of runtime dtype `dt` (RNE rounding).
+__device__ inline void store_elem(void* p, int dt, int64_t idx, float v) {
+  if (dt == F32) {
+    reinterpret_cast<float*>(p)[idx] = v;
+  } else {
+    reinterpret_cast<uint16_t*>(p)[idx] = dt == BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+  }
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Map the
+// hardware id so that each XCD receives a contiguous range of logical ids: consecutive
+// tiles of one matrix then share an L2.
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  constexpr int NXCD = 8;
+  const int q = nblocks / NXCD, r = nblocks % NXCD;
+  const int xcd = bid % NXCD, local = bid / NXCD;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+}  // namespace mns

@@ -1,0 +1,134 @@
+// HBM-bound kernels around the products:
+//  - prep_kernel: reads one 64 x 64 tile of a caller matrix (any dtype/ld/stride), writes it
+//    to the two internal copies the products read (X: n x m row-major, and X^T: m x n
+//    row-major), zero-fills their padded columns, and emits a deterministic per-tile partial
+//    of sum x^2 (the Frobenius norm, guide's normalisation). With momentum enabled it first
+//    applies the Muon momentum rule to the fp32 buffer M and orthogonalizes N instead of G.
+//  - finalize_kernel: sums the partials of one matrix in a fixed order, s = 1/(sqrt + eps),
+//    and writes the per-matrix flags.
+//  - cast_kernel: dtype conversion of an n x ld internal matrix.
+#pragma once
+
+#include "common.hpp"
+
+namespace mns {
+
+struct PrepArgs {
+  const void* G; int g_dt; int64_t ldg, sg;
+  int rows, cols;                      // caller orientation
+  void* out_same; int64_t ld_same, s_same;   // rows x ld_same (pad cols zero)
+  void* out_tr; int64_t ld_tr, s_tr;         // cols x ld_tr   (pad cols zero)
+  int io_dt;
+  double* partials;                    // [batch][tiles]
+  int tiles_x, tiles;                  // tiles_x = ceil(cols/64)
+  // momentum (optional)
+  float* M; int64_t ldm, sm;
+  float mu; int nesterov;
+};
+
+constexpr int PREP_T = 64;
+
+__global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
+  __shared__ float tile[PREP_T][PREP_T + 1];
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  const int mat = blockIdx.y;
+  const int tx = blockIdx.x % p.tiles_x, ty = blockIdx.x / p.tiles_x;
+  const int r0 = ty * PREP_T, c0 = tx * PREP_T;
+  const int es = dtype_size(p.g_dt), ios = dtype_size(p.io_dt);
+  const char* Gb = reinterpret_cast<const char*>(p.G) + (int64_t)mat * p.sg * es;
+  float* Mb = p.M ? p.M + (int64_t)mat * p.sm : nullptr;
+  char* Sb = reinterpret_cast<char*>(p.out_same) + (int64_t)mat * p.s_same * ios;
+  char* Tb = reinterpret_cast<char*>(p.out_tr) + (int64_t)mat * p.s_tr * ios;
+
+  // load: thread -> 4 consecutive columns of rows ty + 16q
+  const int cc = (tid & 15) * 4, rbase = tid >> 4;
+  double ss = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lr = rbase + 16 * q, r = r0 + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c0 + cc + e;
+      float v = 0.f;
+      if (r < p.rows && c < p.cols) {
+        v = load_elem(Gb, p.g_dt, (int64_t)r * p.ldg + c);
+        if (Mb) {
+          const int64_t mi = (int64_t)r * p.ldm + c;
+          const float m = p.mu * Mb[mi] + (1.f - p.mu) * v;
+          Mb[mi] = m;
+          v = p.nesterov ? p.mu * m + (1.f - p.mu) * v : m;
+        }
+        // round to the internal dtype first: the norm is of the values the products read
+        if (p.io_dt == BF16) v = bf16_bits_to_f32(f32_to_bf16_bits(v));
+        else if (p.io_dt == F16) v = f16_bits_to_f32(f32_to_f16_bits(v));
+      }
+      tile[lr][cc + e] = v;
+      ss += (double)v * (double)v;
+    }
+  }
+  __syncthreads();
+  // same orientation: rows r < rows, columns c < ld_same (pad written as zero)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lr = rbase + 16 * q, r = r0 + lr;
+    if (r >= p.rows) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c0 + cc + e;
+      if (c < p.ld_same) store_elem(Sb, p.io_dt, (int64_t)r * p.ld_same + c, tile[lr][cc + e]);
+    }
+  }
+  // transposed: row c (< cols), column r (< ld_tr)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lc = rbase + 16 * q, c = c0 + lc;
+    if (c >= p.cols) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + cc + e;
+      if (r < p.ld_tr) store_elem(Tb, p.io_dt, (int64_t)c * p.ld_tr + r, tile[cc + e][lc]);
+    }
+  }
+  // fixed-order block reduction of the partial sum of squares
+  red[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) p.partials[(int64_t)mat * p.tiles + blockIdx.x] = red[0];
+}
+
+__global__ void __launch_bounds__(256) finalize_kernel(const double* partials, int tiles,
+                                                       float eps, float* svec,
+                                                       int32_t* flags) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x, mat = blockIdx.x;
+  double s = 0.0;
+  for (int i = tid; i < tiles; i += 256) s += partials[(int64_t)mat * tiles + i];
+  red[tid] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (tid < k) red[tid] += red[tid + k];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double ss = red[0];
+    const double nrm = sqrt(ss);
+    svec[mat] = (float)(1.0 / (nrm + (double)eps));
+    if (flags) flags[mat] = (__builtin_isfinite(ss) ? 0 : 1) | (ss == 0.0 ? 2 : 0);
+  }
+}
+
+__global__ void __launch_bounds__(256) cast_kernel(const void* src, int s_dt, void* dst, int d_dt,
+                                                   int64_t per_mat, int64_t s_stride,
+                                                   int64_t d_stride) {
+  const int mat = blockIdx.y;
+  const char* sb = reinterpret_cast<const char*>(src) + (int64_t)mat * s_stride * dtype_size(s_dt);
+  char* db = reinterpret_cast<char*>(dst) + (int64_t)mat * d_stride * dtype_size(d_dt);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per_mat; i += (int64_t)gridDim.x * 256)
+    store_elem(db, d_dt, i, load_elem(sb, s_dt, i));
+}
+
+}  // namespace mns

@@ -1,0 +1,456 @@
+// Batched "NT" matrix product on MFMA for gfx950, with the Newton-Schulz epilogues fused.
+//
+//   C[b][i][j] = sum_k A[b][i][k] * B[b][j][k]     (both operands K-contiguous)
+//
+// Every product of the method has this form:
+//  - X X^T (the Gram / SYRK product): A = B = X (n x m, row-major), K = m;
+//  - products of the symmetric n x n iterates (R R, R Z, Z (R Z), Z Q, A A): the right
+//    operand is symmetric and stored in full, so its rows are its columns;
+//  - the rectangular Q X and B X: the right operand is X^T, kept as an (m x n) row-major
+//    copy whose rows are the columns of X.
+// TRI=true computes only the tiles on or above the diagonal of a symmetric result and
+// writes each value to (i, j) and (j, i), so stored symmetric matrices are exactly
+// symmetric.
+//
+// Tile: 128 x 128 per workgroup of 4 waves (2 x 2), each wave 64 x 64 as 2 x 2 blocks of
+// the 32x32 MFMA (bf16/f16: v_mfma_f32_32x32x16, fp32: v_mfma_f32_32x32x2f32), fp32
+// accumulation. K is staged through LDS 128 bytes per row at a time (64 half-precision or
+// 32 fp32 values), double-buffered, rows padded to 144 bytes so the 16-byte fragment reads
+// of 16 consecutive rows hit distinct banks.
+//
+// Epilogue (per matrix b, scale s_b from the norm kernel):
+//   v = s_b^spow * (c2 * acc + c1 * E[i][j]) + c0 * [i == j < M]
+// then any of: store v to C (i, j) [and (j, i) for TRI], store v to Ct (j, i), and the
+// Muon update W <- wd_mul * W - lr * u_scale * v (optionally U <- u_scale * v).
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace mns {
+
+struct GemmArgs {
+  const void* A; int64_t lda, sA;
+  const void* B; int64_t ldb, sB;
+  int M, N, K;
+  int tiles_m, tiles_n, tiles_per_mat, nblocks, group_m;
+  const float* svec; int spow;
+  float c0, c1, c2;
+  const void* E; int e_dt; int64_t lde, sE; int e_rows, e_cols;
+  void* C; int c_dt; int64_t ldc, sC; int c_rows, c_cols;
+  void* Ct; int ct_dt; int64_t ldct, sCt; int ct_rows, ct_cols;
+  void* W; int w_dt; int64_t ldw, sW; int w_trans;
+  void* U; int u_dt; int64_t ldu, sU;
+  float u_scale, lr, wd_mul;
+  int32_t* flags;
+  // 1 when 8-element vectors of that buffer are aligned (ld, stride and base)
+  int c_vec, ct_vec, w_vec, u_vec;
+};
+
+template <typename T> struct MfmaTraits;
+template <> struct MfmaTraits<__bf16> { static constexpr int ES = 2; };
+template <> struct MfmaTraits<_Float16> { static constexpr int ES = 2; };
+template <> struct MfmaTraits<float> { static constexpr int ES = 4; };
+
+// Tile configuration: BM x BN per workgroup, WVM x WVN waves, each wave (BM/WVM) x (BN/WVN)
+// made of 32 x 32 MFMA blocks. Each k-stage stages KB bytes of every operand row in LDS
+// (KB = 128: 64 half / 32 fp32 values; KB = 64: half that). PF = number of k-stages whose
+// global loads are in flight in registers (1: the next stage, 2: the next two). OCC = waves
+// per SIMD the register budget is sized for.
+template <int BM_, int BN_, int WVM_, int WVN_, int KB_, int PF_, int OCC_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WVM = WVM_, WVN = WVN_, KB = KB_, PF = PF_, OCC = OCC_;
+  static constexpr int NT = 64 * WVM * WVN;
+  static constexpr int WTM = BM / WVM, WTN = BN / WVN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int CPR = KB / 16;                    // 16-byte chunks per staged row
+  static constexpr int NG = KB / 32;                     // 32-byte k-groups per stage (one MFMA k-step)
+  static constexpr int ROWB = KB + 16;                   // LDS bytes per staged row (padded)
+  static constexpr int STAGE = (BM + BN) * ROWB;
+  static constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;  // chunks per thread
+  // Epilogue slab: SR wave-rows of the tile at a time, fp32, rows padded to 16-byte multiples.
+  static constexpr int CP = BN + 4;
+  static constexpr int SR = (WVM >= 4 && BM >= 256) ? 2 : 1;
+  static constexpr int SLAB = SR * WTM * CP * 4;
+  static constexpr int LDS = 2 * STAGE > SLAB ? 2 * STAGE : SLAB;
+  static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile must be whole MFMA blocks");
+  static_assert(CA * NT == BM * CPR && CB * NT == BN * CPR, "chunks must divide evenly");
+  static_assert(NT % CPR == 0, "a thread keeps one chunk column");
+  static_assert(WVM % SR == 0 && BN % 16 == 0 && (SR * WTM) % 32 == 0, "epilogue slab shape");
+};
+
+// Small problems: 128 x 128, 4 waves of 64 x 64, 128-byte k-stages, 2 waves per SIMD.
+// Large problems: 256 x 256, 16 waves of 64 x 64, 128-byte k-stages, 4 waves per SIMD
+// (one workgroup per CU; latency is hidden by the four waves each SIMD interleaves).
+#ifndef MNS_CFG128
+#define MNS_CFG128 128, 128, 2, 2, 128, 1, 2
+#endif
+#ifndef MNS_CFG256
+#define MNS_CFG256 256, 256, 4, 4, 128, 1, 4
+#endif
+using Tile128 = TileCfg<MNS_CFG128>;
+using Tile256 = TileCfg<MNS_CFG256>;
+
+// 8 consecutive elements of a buffer of runtime dtype (16-byte aligned for 16-bit types,
+// 32-byte for fp32).
+__device__ inline void load8(const void* p, int dt, int64_t idx, float (&v)[8]) {
+  if (dt == F32) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + idx);
+    const f32x4 a = q[0], b = q[1];
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p) + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t lo = (uint16_t)(w[e] & 0xffffu), hi = (uint16_t)(w[e] >> 16);
+      v[2 * e] = dt == BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
+      v[2 * e + 1] = dt == BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
+    }
+  }
+}
+
+__device__ inline void store8(void* p, int dt, int64_t idx, const float (&v)[8]) {
+  if (dt == F32) {
+    f32x4* q = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + idx);
+    q[0] = f32x4{v[0], v[1], v[2], v[3]};
+    q[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = dt == BF16 ? f32_to_bf16_bits(v[2 * e]) : f32_to_f16_bits(v[2 * e]);
+      const uint32_t hi = dt == BF16 ? f32_to_bf16_bits(v[2 * e + 1]) : f32_to_f16_bits(v[2 * e + 1]);
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p) + idx) = w;
+  }
+}
+
+// Store elements e in [lo, 8) of a vector at idx: whole vector when allowed, else one by one
+// (only indices below `lim` are written in the scalar path).
+__device__ inline void store_part(void* p, int dt, int64_t idx, const float (&v)[8], int lo,
+                                  int lim, bool vec_ok) {
+  if (lo == 0 && lim >= 8 && vec_ok) {
+    store8(p, dt, idx, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= lo && e < lim) store_elem(p, dt, idx + e, v[e]);
+  }
+}
+
+// MFMA operand fragment of one 32-row block for one 16-byte k-chunk group: 8 half values or
+// 4 fp32 values per lane (lane l holds row l % 32, chunk half l / 32 of the group).
+template <typename T> struct Frag { typedef T type __attribute__((ext_vector_type(8))); };
+template <> struct Frag<float> { typedef f32x4 type; };
+
+template <typename T, int TM, int TN, int ROWB>
+__device__ inline void load_frags(const char* As, const char* Bs, int lane, int g,
+                                  typename Frag<T>::type (&a)[TM], typename Frag<T>::type (&b)[TN]) {
+  typedef typename Frag<T>::type F;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int off = g * 32 + hi * 16;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const F*>(As + (i * 32 + l32) * ROWB + off);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * ROWB + off);
+}
+
+template <typename T, int TM, int TN>
+__device__ inline void mma(const typename Frag<T>::type (&a)[TM], const typename Frag<T>::type (&b)[TN],
+                           f32x16 (&acc)[TM][TN]) {
+  if constexpr (MfmaTraits<T>::ES == 2) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (__is_same(T, __bf16))
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+  } else {
+    // lane (l32, hi) holds k = 4*hi + e of this 8-wide group; A and B agree, so the
+    // products still pair equal k.
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Raw buffer resource over one operand matrix: loads at byte offsets >= num_records return 0,
+// which zero-fills rows past the end and the k tail without branches.
+constexpr uint32_t OOB = 0x80000000u;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <typename T, bool TRI, class CFG>
+__global__ void __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::OCC, CFG::OCC)))
+gemm_nt_kernel(const GemmArgs p) {
+  constexpr int ES = MfmaTraits<T>::ES;
+  constexpr int EPC = 16 / ES;     // elements per 16-byte chunk
+  constexpr int BK = CFG::CPR * EPC;  // elements of K per stage
+  constexpr int BM = CFG::BM, BN = CFG::BN, NT = CFG::NT, ROWB = CFG::ROWB;
+  constexpr int TM = CFG::TM, TN = CFG::TN, WTM = CFG::WTM, WTN = CFG::WTN, CP = CFG::CP;
+  __shared__ __attribute__((aligned(16))) char lds[CFG::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
+
+  const int lid = xcd_remap(blockIdx.x, p.nblocks);
+  const int mat = lid / p.tiles_per_mat;
+  int t = lid - mat * p.tiles_per_mat;
+  int ti, tj;
+  if constexpr (TRI) {
+    const int nt = p.tiles_n;
+    ti = 0;
+    while (t >= nt - ti) { t -= nt - ti; ++ti; }
+    tj = ti + t;
+  } else {
+    // grouped order: consecutive tiles walk down `group_m` tile rows, then move one tile
+    // column right, so concurrently running tiles share both operands' panels in L2
+    const int per = p.group_m * p.tiles_n;
+    const int grp = t / per, first = grp * p.group_m;
+    const int gsz = min(p.group_m, p.tiles_m - first);
+    const int r = t - grp * per;
+    ti = first + r % gsz;
+    tj = r / gsz;
+  }
+  const int row0 = ti * BM, col0 = tj * BN;
+
+  const char* Ab = reinterpret_cast<const char*>(p.A) + (int64_t)mat * p.sA * ES;
+  const char* Bb = reinterpret_cast<const char*>(p.B) + (int64_t)mat * p.sB * ES;
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Ab, (uint32_t)((int64_t)p.M * p.lda * ES));
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bb, (uint32_t)((int64_t)p.N * p.ldb * ES));
+
+  // Global -> register staging, 16-byte chunks: chunk c = tid + NT q covers staged row
+  // c / CPR, bytes 16 (c % CPR) .. +15. Row offsets are fixed per thread; rows past the end
+  // get an out-of-range offset.
+  constexpr int CPR = CFG::CPR, PF = CFG::PF;
+  uint32_t offA[CFG::CA], offB[CFG::CB];
+#pragma unroll
+  for (int q = 0; q < CFG::CA; ++q) {
+    const int c = tid + NT * q, ga = row0 + c / CPR;
+    offA[q] = ga < p.M ? (uint32_t)(ga * p.lda * ES + (c % CPR) * 16) : OOB;
+  }
+#pragma unroll
+  for (int q = 0; q < CFG::CB; ++q) {
+    const int c = tid + NT * q, gb = col0 + c / CPR;
+    offB[q] = gb < p.N ? (uint32_t)(gb * p.ldb * ES + (c % CPR) * 16) : OOB;
+  }
+  const int kc = (tid % CPR) * EPC;  // k offset of this thread's chunks within a stage
+  u32x4 ra[PF][CFG::CA], rb[PF][CFG::CB];
+  const int nk = (p.K + BK - 1) / BK;
+
+  auto load_stage = [&](int k0, int set) {
+    const bool kin = k0 + kc < p.K;
+    const uint32_t kb = (uint32_t)(k0 * ES);
+#pragma unroll
+    for (int q = 0; q < CFG::CA; ++q)
+      ra[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rsA, kin ? offA[q] + kb : OOB, 0, 0);
+#pragma unroll
+    for (int q = 0; q < CFG::CB; ++q)
+      rb[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rsB, kin ? offB[q] + kb : OOB, 0, 0);
+  };
+  auto store_stage = [&](int buf, int set) {
+    char* As_ = lds + buf * CFG::STAGE;
+    char* Bs_ = As_ + BM * ROWB;
+#pragma unroll
+    for (int q = 0; q < CFG::CA; ++q) {
+      const int c = tid + NT * q;
+      *reinterpret_cast<u32x4*>(As_ + (c / CPR) * ROWB + (c % CPR) * 16) = ra[set][q];
+    }
+#pragma unroll
+    for (int q = 0; q < CFG::CB; ++q) {
+      const int c = tid + NT * q;
+      *reinterpret_cast<u32x4*>(Bs_ + (c / CPR) * ROWB + (c % CPR) * 16) = rb[set][q];
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  typedef typename Frag<T>::type F;
+  F fa[2][TM], fb[2][TN];
+  // Prologue: stage 0 in LDS, stages 1 .. PF-1 in flight in register sets 1 .. PF-1.
+#pragma unroll
+  for (int s_ = 0; s_ < PF; ++s_)
+    if (s_ < nk) load_stage(s_ * BK, s_);
+  store_stage(0, 0);
+  __syncthreads();
+
+  // One k-stage: compute from LDS buffer `cur`, prefetch stage kt + PF into register set
+  // kt % PF (freed when stage kt went to LDS), then move stage kt + 1 from its register set
+  // into the other LDS buffer. Register sets are compile-time indices (the loop below is
+  // unrolled by a multiple of PF and 2).
+  auto step = [&](int kt, auto cur_c, auto set_c, auto next_set_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr int set = decltype(set_c)::value;
+    constexpr int nset = decltype(next_set_c)::value;
+    if (kt + PF < nk) load_stage((kt + PF) * BK, set);
+    const char* As = lds + cur * CFG::STAGE + (wm * WTM) * ROWB;
+    const char* Bs = lds + cur * CFG::STAGE + (BM + wn * WTN) * ROWB;
+    load_frags<T, TM, TN, ROWB>(As, Bs, lane, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int g = 0; g < CFG::NG; ++g) {
+      if (g + 1 < CFG::NG) load_frags<T, TM, TN, ROWB>(As, Bs, lane, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+      mma<T, TM, TN>(fa[g & 1], fb[g & 1], acc);
+    }
+    if (kt + 1 < nk) store_stage(cur ^ 1, nset);
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int kt = 0;
+  if constexpr (PF == 1) {
+    for (; kt + 1 < nk; kt += 2) { step(kt, I0{}, I0{}, I0{}); step(kt + 1, I1{}, I0{}, I0{}); }
+    if (kt < nk) step(kt, I0{}, I0{}, I0{});
+  } else if constexpr (PF == 2) {
+    for (; kt + 1 < nk; kt += 2) { step(kt, I0{}, I0{}, I1{}); step(kt + 1, I1{}, I1{}, I0{}); }
+    if (kt < nk) step(kt, I0{}, I0{}, I1{});
+  } else {
+    static_assert(PF == 3, "PF must be 1, 2 or 3");
+    for (; kt + 5 < nk; kt += 6) {
+      step(kt, I0{}, I0{}, I1{}); step(kt + 1, I1{}, I1{}, I2{}); step(kt + 2, I0{}, I2{}, I0{});
+      step(kt + 3, I1{}, I0{}, I1{}); step(kt + 4, I0{}, I1{}, I2{}); step(kt + 5, I1{}, I2{}, I0{});
+    }
+    if (kt < nk) step(kt, I0{}, I0{}, I1{});
+    if (kt + 1 < nk) step(kt + 1, I1{}, I1{}, I2{});
+    if (kt + 2 < nk) step(kt + 2, I0{}, I2{}, I0{});
+    if (kt + 3 < nk) step(kt + 3, I1{}, I0{}, I1{});
+    if (kt + 4 < nk) step(kt + 4, I0{}, I1{}, I2{});
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // A) finish v = s^spow (c2 acc + c1 E) + c0 [i == j] in registers
+  float sc = 1.f;
+  if (p.spow) {
+    const float sb = p.svec[mat];
+    sc = p.spow == 1 ? sb : sb * sb;
+  }
+  const char* Eb = p.E ? reinterpret_cast<const char*>(p.E) + (int64_t)mat * p.sE * dtype_size(p.e_dt) : nullptr;
+  char* Cb = p.C ? reinterpret_cast<char*>(p.C) + (int64_t)mat * p.sC * dtype_size(p.c_dt) : nullptr;
+  char* Ctb = p.Ct ? reinterpret_cast<char*>(p.Ct) + (int64_t)mat * p.sCt * dtype_size(p.ct_dt) : nullptr;
+  char* Wb = p.W ? reinterpret_cast<char*>(p.W) + (int64_t)mat * p.sW * dtype_size(p.w_dt) : nullptr;
+  char* Ub = p.U ? reinterpret_cast<char*>(p.U) + (int64_t)mat * p.sU * dtype_size(p.u_dt) : nullptr;
+  const bool diag = TRI && ti == tj;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int r = row0 + wm * WTM + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const int c = col0 + wn * WTN + j * 32 + (lane & 31);
+        float v = p.c2 * acc[i][j][rr];
+        if (Eb && r < p.e_rows && c < p.e_cols) v += p.c1 * load_elem(Eb, p.e_dt, (int64_t)r * p.lde + c);
+        v *= sc;
+        if (r == c && r < p.M) v += p.c0;
+        if (r < p.M && c < p.N) bad |= !__builtin_isfinite(v);
+        acc[i][j][rr] = v;
+      }
+
+  // B) through LDS SR wave-rows at a time: row-major pass (direct stores, W update) and
+  //    column-major pass (mirror / transposed stores, transposed W update), 8 elements per
+  //    lane and 16-byte accesses where the buffer allows.
+  float* Cs = reinterpret_cast<float*>(lds);
+  constexpr int SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
+  const bool mirror = TRI && Cb;
+  const bool colpass = mirror || Ctb || (Wb && p.w_trans);
+  for (int sl = 0; sl < CFG::WVM / SR; ++sl) {
+    if (wm / SR == sl) {
+      const int lrow0 = (wm % SR) * WTM;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int r = lrow0 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            const int c = wn * WTN + j * 32 + (lane & 31);
+            Cs[r * CP + c] = acc[i][j][rr];
+          }
+    }
+    __syncthreads();
+    const int srow0 = row0 + sl * SROWS;
+    if (Cb || (Wb && !p.w_trans)) {
+      for (int idx = tid; idx < SROWS * VPR; idx += NT) {
+        const int lr = idx / VPR, lc = (idx - lr * VPR) * 8;
+        const int r = srow0 + lr, c = col0 + lc;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(Cs + lr * CP + lc);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(Cs + lr * CP + lc + 4);
+        float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        if (Cb && r < p.c_rows) {
+          const int lo = diag ? max(0, min(8, r - c)) : 0;  // lower-triangle part of a diagonal tile
+          if (lo < 8) store_part(Cb, p.c_dt, (int64_t)r * p.ldc + c, v, lo, p.c_cols - c, p.c_vec);
+        }
+        if (Wb && !p.w_trans && r < p.M) {
+          const int64_t wi = (int64_t)r * p.ldw + c;
+          float w[8], u[8];
+          const int lim = p.N - c;
+          if (lim >= 8 && p.w_vec) load8(Wb, p.w_dt, wi, w);
+          else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = e < lim ? load_elem(Wb, p.w_dt, wi + e) : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { u[e] = p.u_scale * v[e]; w[e] = p.wd_mul * w[e] - p.lr * u[e]; }
+          store_part(Wb, p.w_dt, wi, w, 0, lim, p.w_vec);
+          if (Ub) store_part(Ub, p.u_dt, (int64_t)r * p.ldu + c, u, 0, lim, p.u_vec);
+        }
+      }
+    }
+    if (colpass) {
+      // lanes: 16 columns x 4 row-vectors, so 4 lanes write 64 contiguous bytes of a row of C^T
+      for (int idx = tid; idx < BN * RVC; idx += NT) {
+        const int ci = idx & 15, ri = (idx >> 4) & 3, blk = idx >> 6;
+        const int ncb = BN / 16;
+        const int cb = blk % ncb, rb = blk / ncb;
+        const int lc = cb * 16 + ci, lr = (rb * 4 + ri) * 8;
+        if (lr >= SROWS) continue;
+        const int r = srow0 + lr, c = col0 + lc;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = Cs[(lr + e) * CP + lc];
+        if (mirror && c < p.c_rows) {
+          // element (r + e, c) goes to (c, r + e) when r + e < c on a diagonal tile
+          const int hi = diag ? max(0, min(8, c - r)) : 8;
+          if (hi > 0) store_part(Cb, p.c_dt, (int64_t)c * p.ldc + r, v, 0, min(hi, p.c_cols - r), p.c_vec && hi == 8);
+        }
+        if (Ctb && c < p.ct_rows) store_part(Ctb, p.ct_dt, (int64_t)c * p.ldct + r, v, 0, p.ct_cols - r, p.ct_vec);
+        if (Wb && p.w_trans && c < p.N) {
+          const int64_t wi = (int64_t)c * p.ldw + r;
+          float w[8], u[8];
+          const int lim = p.M - r;
+          if (lim >= 8 && p.w_vec) load8(Wb, p.w_dt, wi, w);
+          else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = e < lim ? load_elem(Wb, p.w_dt, wi + e) : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { u[e] = p.u_scale * v[e]; w[e] = p.wd_mul * w[e] - p.lr * u[e]; }
+          store_part(Wb, p.w_dt, wi, w, 0, lim, p.w_vec);
+          if (Ub) store_part(Ub, p.u_dt, (int64_t)c * p.ldu + r, u, 0, lim, p.u_vec);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (p.flags && bad) atomicOr(p.flags + mat, 4);
+}
+
+}  // namespace mns

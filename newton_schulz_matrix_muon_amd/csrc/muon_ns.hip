@@ -1,0 +1,728 @@
+// libmuon_ns.so: host side of the C ABI declared in include/muon_ns.h.
+//
+// Validation happens before any HIP call. The planner lays out the caller's workspace,
+// splits the batch into chunks that fit, and enqueues, per chunk:
+//   prep (norm partials + the two internal copies of X) -> finalize (scale, flags)
+//   -> the product sequence of the chosen variant (gemm.hpp) with fused epilogues.
+// Everything is asynchronous on the caller's stream; nothing here synchronises.
+
+#include "muon_ns.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+#include "elementwise.hpp"
+#include "gemm.hpp"
+
+using namespace mns;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+// ------------------------------------------------------------------ launch timing
+enum Kind { K_PREP = 0, K_FINALIZE, K_SYRK, K_SYMPROD, K_RECT, K_CAST, NKINDS };
+const char* const kKindNames[NKINDS] = {"prep_norm", "finalize_norm", "gemm_syrk",
+                                        "gemm_symprod", "gemm_rect", "cast"};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[NKINDS];
+  std::vector<hipEvent_t> pool;
+};
+Timing& timing() {
+  static Timing* t = new Timing();  // never destroyed: events may outlive static teardown
+  return *t;
+}
+
+hipEvent_t take_event(Timing& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `f` (which enqueues exactly one kernel on `s`), with events around it when
+// timing is on. Returns MNS_OK or MNS_ERR_HIP.
+template <class F>
+int launch(int kind, hipStream_t s, F&& f) {
+  Timing& t = timing();
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  bool rec = false;
+  {
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (t.on) {
+      e0 = take_event(t);
+      e1 = take_event(t);
+      rec = e0 && e1;
+    }
+  }
+  if (rec) (void)hipEventRecord(e0, s);
+  f();
+  hipError_t err = hipGetLastError();
+  if (rec) {
+    (void)hipEventRecord(e1, s);
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.ev[kind].emplace_back(e0, e1);
+  }
+  if (err != hipSuccess) {
+    g_last_hip = (int)err;
+    return MNS_ERR_HIP;
+  }
+  return MNS_OK;
+}
+
+// ------------------------------------------------------------------ validation helpers
+bool valid_dtype(int dt) { return dt == F32 || dt == BF16 || dt == F16; }
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int check_tensor(const mns_tensor* t, bool need_ptr = true) {
+  if (!t) return MNS_ERR_ARG;
+  if (need_ptr && !t->ptr) return MNS_ERR_ARG;
+  if (!valid_dtype(t->dtype)) return MNS_ERR_DTYPE;
+  if (t->batch < 1 || t->rows < 1 || t->cols < 1) return MNS_ERR_SHAPE;
+  if (t->ld < t->cols) return MNS_ERR_SHAPE;
+  if (t->batch > 1 && t->stride < t->rows * t->ld) return MNS_ERR_SHAPE;
+  // kernel index arithmetic: per-matrix element offsets and dims fit in int32
+  if (t->rows > (1 << 24) || t->cols > (1 << 24) || t->rows * t->ld > INT32_MAX) return MNS_ERR_SHAPE;
+  if (t->batch > (1 << 24)) return MNS_ERR_SHAPE;
+  return MNS_OK;
+}
+
+bool same_shape(const mns_tensor* a, const mns_tensor* b) {
+  return a->batch == b->batch && a->rows == b->rows && a->cols == b->cols;
+}
+
+// byte range [lo, hi) touched by a tensor
+void extent(const mns_tensor* t, uintptr_t* lo, uintptr_t* hi) {
+  const int64_t last = (t->batch - 1) * t->stride + (t->rows - 1) * t->ld + t->cols;
+  *lo = reinterpret_cast<uintptr_t>(t->ptr);
+  *hi = *lo + (uintptr_t)(last * dtype_size(t->dtype));
+}
+
+bool overlap(const mns_tensor* a, const mns_tensor* b) {
+  uintptr_t a0, a1, b0, b1;
+  extent(a, &a0, &a1);
+  extent(b, &b0, &b1);
+  return a0 < b1 && b0 < a1;
+}
+
+struct NsConf {
+  int steps;
+  float coeff[64][3];
+  float eps;
+  int io_dt, it_dt;
+  uint32_t restart;
+};
+
+int check_params(const mns_ns_params* p, int io_dt, NsConf* c) {
+  if (!p) return MNS_ERR_ARG;
+  if (p->steps < 1 || p->steps > 64) return MNS_ERR_ARG;
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return MNS_ERR_ARG;
+  if (!valid_dtype(p->iter_dtype)) return MNS_ERR_DTYPE;
+  if (io_dt == F32 && p->iter_dtype != F32) return MNS_ERR_DTYPE;
+  if (io_dt != F32 && p->iter_dtype == F32) return MNS_ERR_DTYPE;
+  c->steps = p->steps;
+  for (int k = 0; k < p->steps; ++k) {
+    const float dflt[3] = {3.4445f, -4.7750f, 2.0315f};
+    for (int j = 0; j < 3; ++j) {
+      const float v = p->coeffs ? p->coeffs[3 * k + j] : dflt[j];
+      if (!std::isfinite(v)) return MNS_ERR_ARG;
+      c->coeff[k][j] = v;
+    }
+  }
+  c->eps = p->eps;
+  c->io_dt = io_dt;
+  c->it_dt = p->iter_dtype;
+  c->restart = p->restart_mask;
+  return MNS_OK;
+}
+
+// ------------------------------------------------------------------ workspace plan
+struct Geo {
+  int n, m;        // oriented: n <= m
+  bool trans;      // caller matrix is m x n (rows > cols)
+  int64_t ldn, ldm;
+  int prep_tiles, prep_tiles_x;
+};
+
+Geo geometry(const mns_tensor* G) {
+  Geo g;
+  g.trans = G->rows > G->cols;
+  g.n = (int)std::min(G->rows, G->cols);
+  g.m = (int)std::max(G->rows, G->cols);
+  g.ldn = round_up(g.n, 8);
+  g.ldm = round_up(g.m, 8);
+  g.prep_tiles_x = (int)((G->cols + PREP_T - 1) / PREP_T);
+  g.prep_tiles = g.prep_tiles_x * (int)((G->rows + PREP_T - 1) / PREP_T);
+  return g;
+}
+
+struct Buf {
+  size_t off = 0;
+  int64_t per = 0;  // elements per matrix
+  int dt = 0;
+};
+
+struct Layout {
+  size_t total = 0;
+  Buf svec, partials, X0, Xt0, Xt1, X1, A, Bm, R, Z, W, Qa, Qb;
+};
+
+// Restart bits that take effect: steps k = 1 .. K-1 (bit k).
+bool restart_at(const NsConf& c, int k) { return k >= 1 && k < c.steps && k < 32 && ((c.restart >> k) & 1u); }
+bool restarts_used(const NsConf& c) {
+  for (int k = 1; k < c.steps && k < 32; ++k)
+    if (restart_at(c, k)) return true;
+  return false;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout plan(int variant, const Geo& g, const NsConf& c, int64_t chunk) {
+  Layout L;
+  size_t off = 0;
+  auto add = [&](Buf& b, int64_t per, int dt_or_size, bool raw_bytes = false) {
+    b.off = off;
+    b.per = per;
+    b.dt = raw_bytes ? -1 : dt_or_size;
+    const size_t es = raw_bytes ? (size_t)dt_or_size : (size_t)dtype_size(dt_or_size);
+    off = align256(off + (size_t)chunk * (size_t)per * es);
+  };
+  const int io = c.io_dt, it = c.it_dt;
+  const int qdt = dtype_size(io) >= dtype_size(it) ? io : it;
+  add(L.svec, 1, 4, true);
+  add(L.partials, g.prep_tiles, 8, true);
+  add(L.X0, (int64_t)g.n * g.ldm, io);
+  add(L.Xt0, (int64_t)g.m * g.ldn, io);
+  const int64_t nn = (int64_t)g.n * g.ldn;
+  if (variant == MNS_VARIANT_STANDARD) {
+    add(L.X1, (int64_t)g.n * g.ldm, io);
+    add(L.Xt1, (int64_t)g.m * g.ldn, io);
+    add(L.A, nn, it);
+    add(L.Bm, nn, dtype_size(io) >= dtype_size(it) ? io : it);
+  } else {
+    if (restarts_used(c)) add(L.Xt1, (int64_t)g.m * g.ldn, io);
+    add(L.R, nn, it);
+    add(L.Z, nn, it);
+    add(L.W, nn, it);
+    add(L.Qa, nn, qdt);
+    add(L.Qb, nn, qdt);
+  }
+  L.total = off;
+  return L;
+}
+
+template <class T>
+T* at(void* ws, const Buf& b) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + b.off);
+}
+
+int64_t pick_chunk(int variant, const Geo& g, const NsConf& c, int64_t batch, size_t ws_bytes) {
+  const size_t one = plan(variant, g, c, 1).total;
+  if (ws_bytes < one) return 0;
+  const size_t per = plan(variant, g, c, 2).total - one;  // linear growth (+ alignment slack)
+  int64_t b = per ? (int64_t)std::min<size_t>((size_t)batch, 1 + (ws_bytes - one) / per) : batch;
+  b = std::max<int64_t>(1, std::min(b, batch));
+  while (b > 1 && plan(variant, g, c, b).total > ws_bytes) --b;
+  return b;
+}
+
+// ------------------------------------------------------------------ product launcher
+struct Prod {
+  const void* A = nullptr; int64_t lda = 0, sA = 0;
+  const void* B = nullptr; int64_t ldb = 0, sB = 0;
+  int M = 0, N = 0, K = 0, in_dt = 0;
+  bool tri = false;
+  const float* svec = nullptr; int spow = 0;
+  float c0 = 0.f, c1 = 0.f, c2 = 1.f;
+  const void* E = nullptr; int e_dt = 0; int64_t lde = 0, sE = 0; int e_rows = 0, e_cols = 0;
+  void* C = nullptr; int c_dt = 0; int64_t ldc = 0, sC = 0; int c_rows = 0, c_cols = 0;
+  void* Ct = nullptr; int ct_dt = 0; int64_t ldct = 0, sCt = 0; int ct_rows = 0, ct_cols = 0;
+  void* W = nullptr; int w_dt = 0; int64_t ldw = 0, sW = 0; int w_trans = 0;
+  void* U = nullptr; int u_dt = 0; int64_t ldu = 0, sU = 0;
+  float u_scale = 0.f, lr = 0.f, wd_mul = 1.f;
+  int32_t* flags = nullptr;
+};
+
+#ifndef MNS_GROUP_M
+#define MNS_GROUP_M 8
+#endif
+
+template <class CFG>
+int launch_prod(const Prod& q, GemmArgs a, int64_t batch, int kind, hipStream_t s) {
+  const int cover_n = std::max({q.N, q.C ? q.c_cols : 0, q.Ct ? q.ct_rows : 0});
+  const int cover_m = std::max({q.M, q.C ? q.c_rows : 0, q.Ct ? q.ct_cols : 0});
+  const int tm = (cover_m + CFG::BM - 1) / CFG::BM;
+  const int tn = (cover_n + CFG::BN - 1) / CFG::BN;
+  if (q.tri) {
+    const int nt = std::max(tm, tn);
+    a.tiles_m = a.tiles_n = nt;
+    a.tiles_per_mat = nt * (nt + 1) / 2;
+    a.group_m = 1;
+  } else {
+    a.tiles_m = tm;
+    a.tiles_n = tn;
+    a.tiles_per_mat = tm * tn;
+    a.group_m = std::max(1, std::min(tm, MNS_GROUP_M));
+  }
+  const int64_t nb = batch * (int64_t)a.tiles_per_mat;
+  if (nb > INT32_MAX) return MNS_ERR_SHAPE;
+  a.nblocks = (int)nb;
+  dim3 grid(a.nblocks), block(CFG::NT);
+  return launch(kind, s, [&] {
+    if (q.in_dt == BF16) {
+      if (q.tri) hipLaunchKernelGGL((gemm_nt_kernel<__bf16, true, CFG>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((gemm_nt_kernel<__bf16, false, CFG>), grid, block, 0, s, a);
+    } else if (q.in_dt == F16) {
+      if (q.tri) hipLaunchKernelGGL((gemm_nt_kernel<_Float16, true, CFG>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((gemm_nt_kernel<_Float16, false, CFG>), grid, block, 0, s, a);
+    } else {
+      if (q.tri) hipLaunchKernelGGL((gemm_nt_kernel<float, true, CFG>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((gemm_nt_kernel<float, false, CFG>), grid, block, 0, s, a);
+    }
+  });
+}
+
+// Tile choice: the 256 x 256 tile when the product is large enough to fill the chip with it.
+#ifndef MNS_TILE_POLICY
+#define MNS_TILE_POLICY 1
+#endif
+int tile_choice(const Prod& q, int64_t batch) {
+  const int64_t t256 = batch * ((q.M + 255) / 256) * ((q.N + 255) / 256);
+  if (MNS_TILE_POLICY == 0) return 0;
+  if (q.in_dt == F32) return 0;
+  if (q.M < 256 || t256 < 512) return 0;
+  return MNS_TILE_POLICY;
+}
+
+int run_prod(const Prod& q, int64_t batch, int kind, hipStream_t s) {
+  GemmArgs a;
+  a.A = q.A; a.lda = q.lda; a.sA = q.sA;
+  a.B = q.B; a.ldb = q.ldb; a.sB = q.sB;
+  a.M = q.M; a.N = q.N; a.K = q.K;
+  a.svec = q.svec; a.spow = q.spow;
+  a.c0 = q.c0; a.c1 = q.c1; a.c2 = q.c2;
+  a.E = q.E; a.e_dt = q.e_dt; a.lde = q.lde; a.sE = q.sE; a.e_rows = q.e_rows; a.e_cols = q.e_cols;
+  a.C = q.C; a.c_dt = q.c_dt; a.ldc = q.ldc; a.sC = q.sC; a.c_rows = q.c_rows; a.c_cols = q.c_cols;
+  a.Ct = q.Ct; a.ct_dt = q.ct_dt; a.ldct = q.ldct; a.sCt = q.sCt; a.ct_rows = q.ct_rows; a.ct_cols = q.ct_cols;
+  a.W = q.W; a.w_dt = q.w_dt; a.ldw = q.ldw; a.sW = q.sW; a.w_trans = q.w_trans;
+  a.U = q.U; a.u_dt = q.u_dt; a.ldu = q.ldu; a.sU = q.sU;
+  a.u_scale = q.u_scale; a.lr = q.lr; a.wd_mul = q.wd_mul;
+  a.flags = q.flags;
+  auto vec_ok = [&](const void* ptr, int64_t ld, int64_t stride) {
+    return (int)(ptr && ld % 8 == 0 && (batch == 1 || stride % 8 == 0) &&
+                 reinterpret_cast<uintptr_t>(ptr) % 16 == 0);
+  };
+  a.c_vec = vec_ok(q.C, q.ldc, q.sC);
+  a.ct_vec = vec_ok(q.Ct, q.ldct, q.sCt);
+  a.w_vec = vec_ok(q.W, q.ldw, q.sW);
+  a.u_vec = vec_ok(q.U, q.ldu, q.sU);
+  switch (tile_choice(q, batch)) {
+    case 1: return launch_prod<Tile256>(q, a, batch, kind, s);
+    default: return launch_prod<Tile128>(q, a, batch, kind, s);
+  }
+}
+
+// Final destination of the last rectangular product.
+struct FinalOut {
+  const mns_tensor* O = nullptr;      // NS: the output batch
+  const mns_tensor* W = nullptr;      // Muon step: weights (updated)
+  const mns_tensor* U = nullptr;      // Muon step: optional update output
+  float u_scale = 0.f, lr = 0.f, wd_mul = 1.f;
+  int32_t* flags = nullptr;
+};
+
+void set_final(Prod& q, const FinalOut& f, const Geo& g, int64_t b0) {
+  q.flags = f.flags ? f.flags + b0 : nullptr;
+  if (f.O) {
+    const int es = dtype_size(f.O->dtype);
+    void* base = reinterpret_cast<char*>(f.O->ptr) + b0 * f.O->stride * es;
+    if (!g.trans) {
+      q.C = base; q.c_dt = f.O->dtype; q.ldc = f.O->ld; q.sC = f.O->stride;
+      q.c_rows = g.n; q.c_cols = g.m;
+    } else {
+      q.Ct = base; q.ct_dt = f.O->dtype; q.ldct = f.O->ld; q.sCt = f.O->stride;
+      q.ct_rows = g.m; q.ct_cols = g.n;
+    }
+  }
+  if (f.W) {
+    q.W = reinterpret_cast<char*>(f.W->ptr) + b0 * f.W->stride * dtype_size(f.W->dtype);
+    q.w_dt = f.W->dtype; q.ldw = f.W->ld; q.sW = f.W->stride; q.w_trans = g.trans;
+    q.u_scale = f.u_scale; q.lr = f.lr; q.wd_mul = f.wd_mul;
+    if (f.U) {
+      q.U = reinterpret_cast<char*>(f.U->ptr) + b0 * f.U->stride * dtype_size(f.U->dtype);
+      q.u_dt = f.U->dtype; q.ldu = f.U->ld; q.sU = f.U->stride;
+    }
+  }
+}
+
+// Symmetric n x n product C = A . B^T (B symmetric) with the Newton-Schulz epilogue.
+Prod sym_prod(const void* A, const void* B, int in_dt, const Geo& g, void* C, int c_dt) {
+  Prod q;
+  q.A = A; q.lda = g.ldn; q.sA = (int64_t)g.n * g.ldn;
+  q.B = B; q.ldb = g.ldn; q.sB = (int64_t)g.n * g.ldn;
+  q.M = g.n; q.N = g.n; q.K = g.n; q.in_dt = in_dt; q.tri = true;
+  q.C = C; q.c_dt = c_dt; q.ldc = g.ldn; q.sC = (int64_t)g.n * g.ldn;
+  q.c_rows = g.n; q.c_cols = (int)g.ldn;
+  return q;
+}
+
+// Gram product C = s^spow X X^T of the n x m row-major X.
+Prod gram_prod(const void* X, int io_dt, const Geo& g, void* C, int c_dt, const float* svec, int spow) {
+  Prod q;
+  q.A = X; q.lda = g.ldm; q.sA = (int64_t)g.n * g.ldm;
+  q.B = X; q.ldb = g.ldm; q.sB = (int64_t)g.n * g.ldm;
+  q.M = g.n; q.N = g.n; q.K = g.m; q.in_dt = io_dt; q.tri = true;
+  q.C = C; q.c_dt = c_dt; q.ldc = g.ldn; q.sC = (int64_t)g.n * g.ldn;
+  q.c_rows = g.n; q.c_cols = (int)g.ldn;
+  q.svec = svec; q.spow = spow;
+  return q;
+}
+
+// Rectangular C = L . X for an n x n L and X given by its (m x ldn) transposed copy.
+Prod rect_prod(const void* L, const void* Xt, int io_dt, const Geo& g) {
+  Prod q;
+  q.A = L; q.lda = g.ldn; q.sA = (int64_t)g.n * g.ldn;
+  q.B = Xt; q.ldb = g.ldn; q.sB = (int64_t)g.m * g.ldn;
+  q.M = g.n; q.N = g.m; q.K = g.n; q.in_dt = io_dt; q.tri = false;
+  return q;
+}
+
+void set_internal_x_out(Prod& q, void* X, void* Xt, int x_dt, const Geo& g) {
+  q.C = X; q.c_dt = x_dt; q.ldc = g.ldm; q.sC = (int64_t)g.n * g.ldm;
+  q.c_rows = g.n; q.c_cols = (int)g.ldm;
+  q.Ct = Xt; q.ct_dt = x_dt; q.ldct = g.ldn; q.sCt = (int64_t)g.m * g.ldn;
+  q.ct_rows = g.m; q.ct_cols = (int)g.ldn;
+}
+
+struct Source {
+  const mns_tensor* G;
+  const mns_tensor* M = nullptr;  // momentum (muon_step)
+  float mu = 0.f;
+  int nesterov = 0;
+};
+
+int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, void* ws,
+             int64_t b0, int64_t nb, int32_t* flags, hipStream_t s) {
+  const mns_tensor* G = src.G;
+  PrepArgs a;
+  const int es = dtype_size(G->dtype);
+  a.G = reinterpret_cast<const char*>(G->ptr) + b0 * G->stride * es;
+  a.g_dt = G->dtype; a.ldg = G->ld; a.sg = G->stride;
+  a.rows = (int)G->rows; a.cols = (int)G->cols;
+  void* X0 = at<char>(ws, L.X0);
+  void* Xt0 = at<char>(ws, L.Xt0);
+  if (!g.trans) {
+    a.out_same = X0; a.ld_same = g.ldm; a.s_same = (int64_t)g.n * g.ldm;
+    a.out_tr = Xt0; a.ld_tr = g.ldn; a.s_tr = (int64_t)g.m * g.ldn;
+  } else {
+    a.out_same = Xt0; a.ld_same = g.ldn; a.s_same = (int64_t)g.m * g.ldn;
+    a.out_tr = X0; a.ld_tr = g.ldm; a.s_tr = (int64_t)g.n * g.ldm;
+  }
+  a.io_dt = c.io_dt;
+  a.partials = at<double>(ws, L.partials);
+  a.tiles_x = g.prep_tiles_x; a.tiles = g.prep_tiles;
+  a.M = nullptr; a.ldm = 0; a.sm = 0; a.mu = 0.f; a.nesterov = 0;
+  if (src.M) {
+    a.M = reinterpret_cast<float*>(src.M->ptr) + b0 * src.M->stride;
+    a.ldm = src.M->ld; a.sm = src.M->stride; a.mu = src.mu; a.nesterov = src.nesterov;
+  }
+  dim3 grid(g.prep_tiles, (unsigned)nb);
+  int st = launch(K_PREP, s, [&] { hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, s, a); });
+  if (st) return st;
+  double* part = at<double>(ws, L.partials);
+  float* sv = at<float>(ws, L.svec);
+  int32_t* fl = flags ? flags + b0 : nullptr;
+  const int tiles = g.prep_tiles;
+  const float eps = c.eps;
+  return launch(K_FINALIZE, s, [&] {
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)nb), dim3(256), 0, s, part, tiles, eps, sv, fl);
+  });
+}
+
+int run_standard(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b0, int64_t nb,
+                 const FinalOut& fo, hipStream_t s) {
+  const int io = c.io_dt, it = c.it_dt;
+  const float* sv = at<float>(ws, L.svec);
+  char* X[2] = {at<char>(ws, L.X0), at<char>(ws, L.X1)};
+  char* Xt[2] = {at<char>(ws, L.Xt0), at<char>(ws, L.Xt1)};
+  char* A = at<char>(ws, L.A);
+  char* Bm = at<char>(ws, L.Bm);
+  int cur = 0;
+  // X0 is the caller's values in the input dtype; every later X_k is normalised and is
+  // stored in the iterate dtype (fp16 keeps 3 more mantissa bits than bf16 for B X).
+  int xdt = io;
+  for (int k = 1; k <= c.steps; ++k) {
+    const float a_k = c.coeff[k - 1][0], b_k = c.coeff[k - 1][1], c_k = c.coeff[k - 1][2];
+    const bool first = k == 1;
+    // A = X X^T (scaled by s^2 on the unnormalised first iterate)
+    Prod q = gram_prod(X[cur], xdt, g, A, it, sv, first ? 2 : 0);
+    if (int st = run_prod(q, nb, K_SYRK, s)) return st;
+    // B = b A + c A^2, stored in the dtype of X (the two are the operands of B X)
+    q = sym_prod(A, A, it, g, Bm, xdt);
+    q.c0 = 0.f; q.c1 = b_k; q.c2 = c_k;
+    q.E = A; q.e_dt = it; q.lde = g.ldn; q.sE = (int64_t)g.n * g.ldn; q.e_rows = g.n; q.e_cols = (int)g.ldn;
+    if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+    // X <- s (a X + B X)
+    q = rect_prod(Bm, Xt[cur], xdt, g);
+    q.svec = sv; q.spow = first ? 1 : 0;
+    q.c1 = a_k; q.c2 = 1.f;
+    q.E = X[cur]; q.e_dt = xdt; q.lde = g.ldm; q.sE = (int64_t)g.n * g.ldm; q.e_rows = g.n; q.e_cols = (int)g.ldm;
+    if (k < c.steps) set_internal_x_out(q, X[cur ^ 1], Xt[cur ^ 1], it, g);
+    else set_final(q, fo, g, b0);
+    if (int st = run_prod(q, nb, K_RECT, s)) return st;
+    cur ^= 1;
+    xdt = it;
+  }
+  return MNS_OK;
+}
+
+int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b0, int64_t nb,
+             const FinalOut& fo, hipStream_t s) {
+  const int io = c.io_dt, it = c.it_dt;
+  const float* sv = at<float>(ws, L.svec);
+  char* Xrow = at<char>(ws, L.X0);                       // n x ldm, overwritten at restarts
+  char* Xtb[2] = {at<char>(ws, L.Xt0), L.Xt1.per ? at<char>(ws, L.Xt1) : nullptr};
+  int xt = 0;
+  char* R = at<char>(ws, L.R);
+  char* Z = at<char>(ws, L.Z);
+  char* Wb = at<char>(ws, L.W);
+  char* Qbuf[2] = {at<char>(ws, L.Qa), at<char>(ws, L.Qb)};
+  int xspow = 1;  // the current X is the unnormalised input: scale by s once
+  int xdt = io;   // dtype of the current X; normalised restarts store it in the iterate dtype
+  const int64_t nn = (int64_t)g.n * g.ldn;
+
+  Prod q = gram_prod(Xrow, xdt, g, R, it, sv, 2);
+  if (int st = run_prod(q, nb, K_SYRK, s)) return st;
+
+  bool q_fresh = true;
+  int qcur = 0;
+  for (int k = 1; k <= c.steps; ++k) {
+    const float a_k = c.coeff[k - 1][0], b_k = c.coeff[k - 1][1], c_k = c.coeff[k - 1][2];
+    const bool restart = restart_at(c, k);
+    const bool need_rect = restart || k == c.steps;
+    // Z = a I + b R + c R^2
+    char* zdst;
+    int zdt = it;
+    if (q_fresh) {
+      zdst = Qbuf[0];
+      zdt = need_rect ? xdt : it;
+    } else {
+      zdst = Z;
+    }
+    q = sym_prod(R, R, it, g, zdst, zdt);
+    q.c0 = a_k; q.c1 = b_k; q.c2 = c_k;
+    q.E = R; q.e_dt = it; q.lde = g.ldn; q.sE = nn; q.e_rows = g.n; q.e_cols = (int)g.ldn;
+    if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+    if (q_fresh) {
+      qcur = 0;
+      q_fresh = false;
+    } else {
+      const int nxt = qcur ^ 1;
+      q = sym_prod(Z, Qbuf[qcur], it, g, Qbuf[nxt], need_rect ? xdt : it);
+      if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+      qcur = nxt;
+    }
+    if (restart) {
+      // X <- Q X (explicit), R <- X X^T, Q <- I
+      q = rect_prod(Qbuf[qcur], Xtb[xt], xdt, g);
+      q.svec = sv; q.spow = xspow;
+      set_internal_x_out(q, Xrow, Xtb[xt ^ 1], it, g);
+      if (int st = run_prod(q, nb, K_RECT, s)) return st;
+      xt ^= 1;
+      xspow = 0;
+      xdt = it;
+      q = gram_prod(Xrow, xdt, g, R, it, sv, 0);
+      if (int st = run_prod(q, nb, K_SYRK, s)) return st;
+      q_fresh = true;
+    } else if (k < c.steps) {
+      // W = R Z, R <- Z W
+      q = sym_prod(R, zdst, it, g, Wb, it);
+      if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+      q = sym_prod(zdst, Wb, it, g, R, it);
+      if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+    }
+  }
+  // output = s^xspow Q X
+  q = rect_prod(Qbuf[qcur], Xtb[xt], xdt, g);
+  q.svec = sv; q.spow = xspow;
+  set_final(q, fo, g, b0);
+  return run_prod(q, nb, K_RECT, s);
+}
+
+int run_ns(int variant, const Source& src, const FinalOut& fo, const NsConf& c, void* ws,
+           size_t ws_bytes, int32_t* flags, hipStream_t s) {
+  const Geo g = geometry(src.G);
+  const int64_t batch = src.G->batch;
+  const int64_t chunk = pick_chunk(variant, g, c, batch, ws_bytes);
+  if (chunk < 1) return MNS_ERR_WORKSPACE;
+  const Layout L = plan(variant, g, c, chunk);
+  for (int64_t b0 = 0; b0 < batch; b0 += chunk) {
+    const int64_t nb = std::min(chunk, batch - b0);
+    if (int st = run_prep(src, g, c, L, ws, b0, nb, flags, s)) return st;
+    FinalOut f = fo;
+    f.flags = flags;
+    int st = variant == MNS_VARIANT_STANDARD ? run_standard(g, c, L, ws, b0, nb, f, s)
+                                             : run_gram(g, c, L, ws, b0, nb, f, s);
+    if (st) return st;
+  }
+  return MNS_OK;
+}
+
+int ns_entry(int variant, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+             void* ws, size_t ws_bytes, int32_t* flags, void* stream) {
+  if (int st = check_tensor(G)) return st;
+  if (int st = check_tensor(O)) return st;
+  if (!same_shape(G, O)) return MNS_ERR_SHAPE;
+  if (O->dtype != G->dtype) return MNS_ERR_DTYPE;
+  if (overlap(G, O)) return MNS_ERR_ARG;
+  NsConf c;
+  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (!ws) return MNS_ERR_WORKSPACE;
+  Source src;
+  src.G = G;
+  FinalOut fo;
+  fo.O = O;
+  return run_ns(variant, src, fo, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+int mns_workspace_bytes(int variant, const mns_tensor* G, const mns_ns_params* p,
+                        int64_t max_batch_chunk, size_t* bytes) {
+  if (!bytes) return MNS_ERR_ARG;
+  if (variant != MNS_VARIANT_STANDARD && variant != MNS_VARIANT_GRAM) return MNS_ERR_ARG;
+  if (int st = check_tensor(G, false)) return st;
+  NsConf c;
+  if (int st = check_params(p, G->dtype, &c)) return st;
+  const int64_t chunk = max_batch_chunk <= 0 ? G->batch : std::min(max_batch_chunk, G->batch);
+  *bytes = plan(variant, geometry(G), c, chunk).total;
+  return MNS_OK;
+}
+
+int muon_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,
+                    size_t ws_bytes, int32_t* flags, void* stream) {
+  return ns_entry(MNS_VARIANT_STANDARD, G, O, p, ws, ws_bytes, flags, stream);
+}
+
+int gram_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,
+                    size_t ws_bytes, int32_t* flags, void* stream) {
+  return ns_entry(MNS_VARIANT_GRAM, G, O, p, ws, ws_bytes, flags, stream);
+}
+
+int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, const mns_tensor* U_out,
+              const mns_step_params* sp, const mns_ns_params* p, void* ws, size_t ws_bytes,
+              int32_t* flags, void* stream) {
+  if (int st = check_tensor(W)) return st;
+  if (int st = check_tensor(G)) return st;
+  if (int st = check_tensor(M)) return st;
+  if (!sp) return MNS_ERR_ARG;
+  if (!same_shape(W, G) || !same_shape(M, G)) return MNS_ERR_SHAPE;
+  if (M->dtype != F32) return MNS_ERR_DTYPE;
+  if (U_out) {
+    if (int st = check_tensor(U_out)) return st;
+    if (!same_shape(U_out, G)) return MNS_ERR_SHAPE;
+    if (overlap(U_out, W) || overlap(U_out, G) || overlap(U_out, M)) return MNS_ERR_ARG;
+  }
+  if (overlap(W, G) || overlap(W, M) || overlap(G, M)) return MNS_ERR_ARG;
+  if (sp->variant != MNS_VARIANT_STANDARD && sp->variant != MNS_VARIANT_GRAM) return MNS_ERR_ARG;
+  const float vals[4] = {sp->lr, sp->momentum, sp->weight_decay, sp->scale_coeff};
+  for (float v : vals)
+    if (!std::isfinite(v)) return MNS_ERR_ARG;
+  NsConf c;
+  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (!ws) return MNS_ERR_WORKSPACE;
+  Source src;
+  src.G = G;
+  src.M = M;
+  src.mu = sp->momentum;
+  src.nesterov = sp->nesterov ? 1 : 0;
+  FinalOut fo;
+  fo.W = W;
+  fo.U = U_out;
+  fo.u_scale = sp->scale_coeff * (float)std::sqrt((double)std::max(W->rows, W->cols));
+  fo.lr = sp->lr;
+  fo.wd_mul = (float)(1.0 - (double)sp->lr * (double)sp->weight_decay);
+  return run_ns(sp->variant, src, fo, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char* mns_status_string(int code) {
+  switch (code) {
+    case MNS_OK: return "ok";
+    case MNS_ERR_ARG: return "invalid argument";
+    case MNS_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MNS_ERR_SHAPE: return "invalid or mismatched shape";
+    case MNS_ERR_WORKSPACE: return "workspace missing or too small";
+    case MNS_ERR_HIP: return "HIP runtime error";
+    case MNS_ERR_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+int mns_last_hip_error(void) { return g_last_hip; }
+
+int mns_version(void) { return 100; }
+
+int mns_timing_enable(int on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return MNS_OK;
+}
+
+int mns_timing_reset(void) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& v : t.ev) {
+    for (auto& pr : v) {
+      t.pool.push_back(pr.first);
+      t.pool.push_back(pr.second);
+    }
+    v.clear();
+  }
+  return MNS_OK;
+}
+
+int mns_timing_query(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= NKINDS || !total_ms || !launches) return MNS_ERR_ARG;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  double tot = 0.0;
+  for (auto& pr : t.ev[kind]) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) {
+      g_last_hip = (int)e;
+      return MNS_ERR_HIP;
+    }
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)t.ev[kind].size();
+  return MNS_OK;
+}
+
+int mns_timing_kinds(void) { return NKINDS; }
+
+const char* mns_kernel_kind_name(int kind) {
+  return (kind >= 0 && kind < NKINDS) ? kKindNames[kind] : nullptr;
+}
+
+}  // extern "C"

@@ -1,0 +1,234 @@
+"""Thin ctypes binding of libmuon_ns.so (include/muon_ns.h).
+
+Argument marshalling only: torch tensors are described to the C ABI by pointer, dtype,
+shape and strides, the workspace is a torch allocation, and the stream is torch's
+current stream. Every step of the computation runs in the library's HIP kernels. If the
+library is missing this module raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmuon_ns.so")
+
+F32, BF16, F16 = 0, 1, 2
+STANDARD, GRAM = 0, 1
+STATUS = {0: "MNS_OK", -1: "MNS_ERR_ARG", -2: "MNS_ERR_DTYPE", -3: "MNS_ERR_SHAPE",
+          -4: "MNS_ERR_WORKSPACE", -5: "MNS_ERR_HIP", -6: "MNS_ERR_UNSUPPORTED"}
+
+# Defaults of the guide's optimizer listing (lr, momentum, weight decay, steps, eps).
+DEFAULT_STEPS = 5
+DEFAULT_EPS = 1e-7
+STABILIZED_RESTART_MASK = 1 << 2
+
+
+class MnsTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64),
+                ("stride", ctypes.c_int64)]
+
+
+class MnsNsParams(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int32), ("coeffs", ctypes.POINTER(ctypes.c_float)),
+                ("eps", ctypes.c_float), ("iter_dtype", ctypes.c_int32),
+                ("restart_mask", ctypes.c_uint32)]
+
+
+class MnsStepParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("scale_coeff", ctypes.c_float),
+                ("nesterov", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+
+class MnsError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({_lib().mns_status_string(code).decode()})"
+                         + (f", hipError {_lib().mns_last_hip_error()}" if code == -5 else ""))
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m newton_schulz_matrix_muon_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.mns_workspace_bytes.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsNsParams),
+                                            ctypes.c_int64, P(sz)]
+        for fn in (lib.muon_ns_batched, lib.gram_ns_batched):
+            fn.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
+        lib.muon_step.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
+                                  P(MnsStepParams), P(MnsNsParams), vp, sz, vp, vp]
+        lib.mns_status_string.argtypes = [ctypes.c_int]
+        lib.mns_status_string.restype = ctypes.c_char_p
+        lib.mns_last_hip_error.argtypes = []
+        lib.mns_version.argtypes = []
+        lib.mns_timing_enable.argtypes = [ctypes.c_int]
+        lib.mns_timing_reset.argtypes = []
+        lib.mns_timing_query.argtypes = [ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]
+        lib.mns_timing_kinds.argtypes = []
+        lib.mns_kernel_kind_name.argtypes = [ctypes.c_int]
+        lib.mns_kernel_kind_name.restype = ctypes.c_char_p
+        for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched,
+                  lib.muon_step, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
+                  lib.mns_timing_reset, lib.mns_timing_query, lib.mns_timing_kinds):
+            f.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it has not been built)."""
+    return _lib()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise MnsError(code, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def describe(t) -> MnsTensor:
+    """mns_tensor for a 2-D (one matrix) or 3-D (batch) tensor with unit column stride."""
+    if t.dim() == 2:
+        t3 = t.unsqueeze(0)
+    elif t.dim() == 3:
+        t3 = t
+    else:
+        raise ValueError("expected a 2-D matrix or a 3-D batch")
+    if t3.stride(-1) != 1:
+        raise ValueError("rows must be contiguous (stride(-1) == 1)")
+    b, r, c = t3.shape
+    ld = t3.stride(-2) if r > 1 else c
+    stride = t3.stride(0) if b > 1 else r * ld
+    return MnsTensor(t3.data_ptr(), dtype_code(t3), b, r, c, ld, stride)
+
+
+def ns_params(steps: int = DEFAULT_STEPS, coeffs: Optional[Sequence] = None,
+              eps: float = DEFAULT_EPS, iter_dtype: Optional[int] = None, io_dtype: int = BF16,
+              restart_mask: int = STABILIZED_RESTART_MASK):
+    keep = None
+    cptr = None
+    if coeffs is not None:
+        flat = []
+        for row in coeffs:
+            flat.extend(float(v) for v in row)
+        if len(flat) != 3 * steps:
+            raise ValueError("coeffs must hold one (a, b, c) triple per step")
+        keep = (ctypes.c_float * len(flat))(*flat)
+        cptr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    if iter_dtype is None:
+        iter_dtype = F32 if io_dtype == F32 else F16
+    p = MnsNsParams(steps, cptr, eps, iter_dtype, restart_mask)
+    p._keep = keep  # keep the coefficient array alive with the struct
+    return p
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def workspace_bytes(variant: int, G, params: MnsNsParams, max_batch_chunk: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib().mns_workspace_bytes(variant, ctypes.byref(describe(G)), ctypes.byref(params),
+                                      max_batch_chunk, ctypes.byref(out)), "mns_workspace_bytes")
+    return out.value
+
+
+def _workspace(variant, G, params, workspace):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(variant, G, params), dtype=torch.uint8,
+                                device=G.device)
+    return workspace
+
+
+def _ns(variant, G, out, params, workspace, flags):
+    torch = _torch()
+    if not G.is_cuda:
+        raise ValueError("G must be a device tensor")
+    out = torch.empty_like(G) if out is None else out
+    ws = _workspace(variant, G, params, workspace)
+    fn = _lib().muon_ns_batched if variant == STANDARD else _lib().gram_ns_batched
+    fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
+    _check(fn(ctypes.byref(describe(G)), ctypes.byref(describe(out)), ctypes.byref(params),
+              ctypes.c_void_p(ws.data_ptr()), ws.numel(), fptr, _stream_ptr(G)),
+           "muon_ns_batched" if variant == STANDARD else "gram_ns_batched")
+    return out
+
+
+def muon_ns(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+            iter_dtype: Optional[int] = None, out=None, workspace=None, flags=None):
+    """Standard Newton-Schulz of a matrix or batch (C ABI ``muon_ns_batched``)."""
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G), 0)
+    return _ns(STANDARD, G, out, p, workspace, flags)
+
+
+def gram_ns(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+            iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK,
+            out=None, workspace=None, flags=None):
+    """Gram Newton-Schulz (C ABI ``gram_ns_batched``); restart_mask=0 is the naive variant."""
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G), restart_mask)
+    return _ns(GRAM, G, out, p, workspace, flags)
+
+
+def muon_step(W, G, M, *, lr: float, momentum: float, weight_decay: float,
+              scale_coeff: float = 0.2, nesterov: bool = False, variant: int = GRAM,
+              steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+              iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK,
+              U_out=None, workspace=None, flags=None):
+    """One fused Muon step (C ABI ``muon_step``); W and M are updated in place."""
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G),
+                  restart_mask if variant == GRAM else 0)
+    sp = MnsStepParams(lr, momentum, weight_decay, scale_coeff, 1 if nesterov else 0, variant)
+    ws = _workspace(variant, G, p, workspace)
+    fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
+    u = ctypes.byref(describe(U_out)) if U_out is not None else None
+    _check(_lib().muon_step(ctypes.byref(describe(W)), ctypes.byref(describe(G)),
+                            ctypes.byref(describe(M)), u, ctypes.byref(sp), ctypes.byref(p),
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), fptr, _stream_ptr(G)),
+           "muon_step")
+    return W
+
+
+# ------------------------------------------------------------------ launch timing
+
+def timing_enable(on: bool = True):
+    _check(_lib().mns_timing_enable(1 if on else 0), "mns_timing_enable")
+
+
+def timing_reset():
+    _check(_lib().mns_timing_reset(), "mns_timing_reset")
+
+
+def timing_query() -> dict:
+    """{kind_name: (total_ms, launches)} over the events recorded since the last reset."""
+    L = _lib()
+    out = {}
+    for k in range(L.mns_timing_kinds()):
+        ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+        _check(L.mns_timing_query(k, ctypes.byref(ms), ctypes.byref(n)), "mns_timing_query")
+        out[L.mns_kernel_kind_name(k).decode()] = (ms.value, n.value)
+    return out

@@ -14,6 +14,7 @@ from .ns import (  # noqa: F401
     ns_standard,
     ns_gram,
     ns_svd_closed_form,
+    ns_closed_form_entries,
     scalar_ns_map,
     muon_step,
 )

@@ -151,6 +151,18 @@ def ns_svd_closed_form(G, coeffs=None, eps: float = 1e-7, steps: Optional[int] =
     return (U * scalar_ns_map(s / nrm, coeffs, steps)) @ Vt
 
 
+def ns_closed_form_entries(U_rows, spectrum, V_rows, coeffs=None, eps: float = 1e-7,
+                           steps: Optional[int] = None, fro_norm: Optional[float] = None) -> np.ndarray:
+    """Selected entries of the output for an input with a known SVD G = U diag(spectrum) V^T:
+    rows i of U (``U_rows``, k x r) and rows j of V (``V_rows``, l x r) give the k x l block
+    U_rows diag(p_K(...p_1(spectrum / (||G||_F + eps)))) V_rows^T. ``fro_norm`` defaults to
+    ||spectrum||_2 (= ||G||_F)."""
+    s = np.asarray(spectrum, dtype=np.float64)
+    nrm = float(np.linalg.norm(s)) if fro_norm is None else float(fro_norm)
+    f = scalar_ns_map(s / (nrm + eps), coeffs, steps)
+    return (np.asarray(U_rows, dtype=np.float64) * f) @ np.asarray(V_rows, dtype=np.float64).T
+
+
 def muon_step(W, G, M, lr: float, momentum: float, weight_decay: float,
               nesterov: bool = False, scale_coeff: float = 0.2,
               ns: Optional[Callable] = None):

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every entry point the header declares, and rejects bad
+arguments on the host before any HIP call (no GPU is needed for these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_ns.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from newton_schulz_matrix_muon_amd import ops
+    return ops.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("muon_ns_batched", "gram_ns_batched", "muon_step", "mns_workspace_bytes",
+              "mns_status_string", "mns_last_hip_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    for code in (0, -1, -2, -3, -4, -5, -6, 12345):
+        assert L.mns_status_string(code)
+    assert L.mns_version() >= 100
+    assert L.mns_last_hip_error() == 0
+
+
+def _t(ops, ptr=0x10000, dtype=1, batch=2, rows=8, cols=16, ld=None, stride=None):
+    ld = cols if ld is None else ld
+    stride = rows * ld if stride is None else stride
+    return ops.MnsTensor(ptr, dtype, batch, rows, cols, ld, stride)
+
+
+def test_workspace_query_is_host_only_and_monotone(L):
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    G = _t(ops, batch=648, rows=2048, cols=7168)
+    out = {}
+    for variant in (ops.STANDARD, ops.GRAM):
+        b1, ball = ctypes.c_size_t(), ctypes.c_size_t()
+        assert L.mns_workspace_bytes(variant, ctypes.byref(G), ctypes.byref(p), 1, ctypes.byref(b1)) == 0
+        assert L.mns_workspace_bytes(variant, ctypes.byref(G), ctypes.byref(p), 0, ctypes.byref(ball)) == 0
+        assert 100e6 < b1.value < 200e6 and ball.value > 600 * b1.value
+        out[variant] = b1.value
+    # transposed orientation needs the same space
+    Gt = _t(ops, batch=648, rows=7168, cols=2048)
+    bt = ctypes.c_size_t()
+    assert L.mns_workspace_bytes(ops.GRAM, ctypes.byref(Gt), ctypes.byref(p), 1, ctypes.byref(bt)) == 0
+    assert bt.value == out[ops.GRAM]
+
+
+def test_argument_errors_return_before_any_hip_call(L):
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    G = _t(ops, ptr=0x10000)
+    O = _t(ops, ptr=0x90000000)
+    ws = ctypes.c_void_p(0x7f0000000000)
+    call = lambda g, o, pp=p, w=ws, nb=1 << 40: L.gram_ns_batched(
+        ctypes.byref(g), ctypes.byref(o), ctypes.byref(pp), w, nb, None, None)
+    assert call(G, O, w=None) == -4                                    # no workspace
+    assert call(G, O, nb=16) == -4                                     # too small
+    assert call(_t(ops, ptr=0), O) == -1                               # null input
+    assert call(_t(ops, rows=0), O) == -3                              # empty
+    assert call(_t(ops, ld=4), O) == -3                                # ld < cols
+    assert call(_t(ops, stride=10), O) == -3                           # stride too small
+    assert call(_t(ops, dtype=7), O) == -2                             # unknown dtype
+    assert call(G, _t(ops, ptr=0x90000000, dtype=2)) == -2             # out dtype differs
+    assert call(G, _t(ops, ptr=0x90000000, cols=15)) == -3             # shape mismatch
+    assert call(G, _t(ops, ptr=0x10000 + 64)) == -1                    # overlap
+    bad = ops.ns_params(steps=0, io_dtype=ops.BF16)
+    assert call(G, O, pp=bad) == -1
+    bad = ops.ns_params(io_dtype=ops.BF16, iter_dtype=ops.F32)        # fp32 iterates need fp32 input
+    assert call(G, O, pp=bad) == -2
+    bad = ops.ns_params(coeffs=[[float("nan"), 0, 0]] * 5, io_dtype=ops.BF16)
+    assert call(G, O, pp=bad) == -1
+    assert L.mns_last_hip_error() == 0
+
+
+def test_muon_step_argument_errors(L):
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    sp = ops.MnsStepParams(0.02, 0.95, 0.01, 0.2, 1, ops.GRAM)
+    W = _t(ops, ptr=0x100000)
+    G = _t(ops, ptr=0x200000)
+    M = _t(ops, ptr=0x300000, dtype=0)
+    ws = ctypes.c_void_p(0x7f0000000000)
+    f = lambda w=W, g=G, m=M, s=sp, wsp=ws: L.muon_step(
+        ctypes.byref(w), ctypes.byref(g), ctypes.byref(m), None, ctypes.byref(s),
+        ctypes.byref(p), wsp, 1 << 40, None, None)
+    assert f(wsp=None) == -4
+    assert f(m=_t(ops, ptr=0x300000, dtype=1)) == -2                  # momentum must be fp32
+    assert f(w=_t(ops, ptr=0x100000, rows=9)) == -3
+    assert f(g=_t(ops, ptr=0x100000 + 32)) == -1                      # W and G overlap
+    assert f(s=ops.MnsStepParams(float("inf"), 0.95, 0.01, 0.2, 1, ops.GRAM)) == -1
+    assert f(s=ops.MnsStepParams(0.02, 0.95, 0.01, 0.2, 1, 5)) == -1
+
+
+def test_timing_api_without_launches(L):
+    from newton_schulz_matrix_muon_amd import ops
+    names = [L.mns_kernel_kind_name(k).decode() for k in range(L.mns_timing_kinds())]
+    assert {"gemm_rect", "gemm_symprod", "gemm_syrk", "prep_norm"} <= set(names)
+    assert L.mns_kernel_kind_name(99) is None
+    ops.timing_reset()
+    assert all(v == (0.0, 0) for v in ops.timing_query().values())

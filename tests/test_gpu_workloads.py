@@ -1,0 +1,143 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench uses.
+
+* expert batch 64 x 1408 x 2048 bf16: two fused Muon steps (Nesterov, mu 0.95, lr 2e-4,
+  wd 0.1, scale 0.2 sqrt(2048)); sampled matrices checked against the oracle.
+* Kimi-K2 expert batch 648 x 2048 x 7168 bf16 (the bench's workload, whole batch in one
+  workspace chunk): sampled matrices against the oracle for both variants.
+* Kimi-K2 dense 3 x 7168 x 18432 bf16: a power-law input with a known SVD built from
+  Kronecker products of small orthogonal factors; sampled output entries against the
+  closed form U p(S) V^T (a property that holds at any size).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import band_ok, bf16_steps, rel_fro, say, to_np, w_update_ok
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from newton_schulz_matrix_muon_amd import ops as o
+    o.lib()
+    return o
+
+
+@pytest.mark.parametrize("variant", ["standard", "gram_stabilized"])
+def test_expert_batch_1408x2048_muon_step(torch, ops, variant):
+    say(f"case expert 64x1408x2048 muon_step {variant}")
+    B, r, c = 64, 1408, 2048
+    code = ops.GRAM if variant == "gram_stabilized" else ops.STANDARD
+    ns = (lambda x: oracle.ns_gram(x, restarts=(2,))) if code == ops.GRAM else oracle.ns_standard
+    W = synth.torch_weights(B, r, c, workload_index=1, device="cuda")
+    M = torch.zeros(B, r, c, dtype=torch.float32, device="cuda")
+    U = torch.empty(B, r, c, dtype=torch.float32, device="cuda")
+    lr, mu, wd = 2e-4, 0.95, 0.1
+    picks = [0, 37, 63]
+    Wh = {b: to_np(W[b]) for b in picks}
+    Mh = {b: np.zeros((r, c)) for b in picks}
+    for step in range(2):
+        G = synth.torch_lowrank_plus_noise(B, r, c, power=0.7, noise=0.05, workload_index=1,
+                                           seed_offset=1000 * step, device="cuda")
+        ops.muon_step(W, G, M, lr=lr, momentum=mu, weight_decay=wd, nesterov=True,
+                      scale_coeff=0.2, variant=code, U_out=U)
+        torch.cuda.synchronize()
+        for b in picks:
+            Wn, Mn, Un = oracle.muon_step(Wh[b], to_np(G[b]), Mh[b], lr, mu, wd, nesterov=True,
+                                          scale_coeff=0.2, ns=ns)
+            Ug, Wg, Mg = to_np(U[b]), to_np(W[b]), to_np(M[b])
+            e = rel_fro(Ug, Un)
+            ok, info = band_ok(Ug, Un, TOL)
+            say(f"  step {step} matrix {b}: U rel_F {e:.3e}, band {info}")
+            assert e <= TOL and ok
+            assert rel_fro(Mg, Mn) < 1e-6
+            # bf16 weights: the update applied to the returned U, rounded once ...
+            ok, frac = w_update_ok(Wg, Wh[b], Ug, lr, wd, "bf16")
+            assert ok, f"W update off at step {step}: {frac:.2e} of entries"
+            # ... and the oracle's weights up to one bf16 step plus lr |U - U_oracle| (the
+            # update's own deviation, bounded by the U check above)
+            ulp = np.spacing(np.abs(Wn).astype(np.float32)).astype(np.float64) * 2 ** 16
+            dev = np.abs(Wg - Wn) - lr * np.abs(Ug - Un)
+            say(f"    W: {np.mean(bf16_steps(Wg, Wn) == 0):.4f} of entries equal to the oracle's rounded W")
+            assert np.all(dev <= ulp + 1e-12)
+            Wh[b], Mh[b] = Wg, Mg
+
+
+def test_k2_expert_batch_648x2048x7168_sampled(torch, ops):
+    B, r, c = 648, 2048, 7168
+    say(f"case k2 experts {B}x{r}x{c}: generating")
+    G = synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device="cuda")
+    p_g = ops.ns_params(io_dtype=ops.BF16, restart_mask=1 << 2)
+    p_s = ops.ns_params(io_dtype=ops.BF16, restart_mask=0)
+    ws = torch.empty(max(ops.workspace_bytes(ops.GRAM, G, p_g),
+                         ops.workspace_bytes(ops.STANDARD, G, p_s)), dtype=torch.uint8, device="cuda")
+    O = torch.empty_like(G)
+    flags = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    picks = [0, 647]
+    Gh = {b: to_np(G[b]) for b in picks}
+    for variant in ("gram_stabilized", "standard"):
+        say(f"  running {variant} on the whole batch")
+        if variant == "standard":
+            ops.muon_ns(G, out=O, workspace=ws, flags=flags)
+            ref_fn = oracle.ns_standard
+        else:
+            ops.gram_ns(G, out=O, workspace=ws, flags=flags)
+            ref_fn = lambda x: oracle.ns_gram(x, restarts=(2,))
+        torch.cuda.synchronize()
+        assert int(flags.abs().sum()) == 0, "flags raised"
+        assert bool(torch.isfinite(O.float()).all())
+        for b in picks:
+            ref = ref_fn(Gh[b])
+            got = to_np(O[b])
+            e = rel_fro(got, ref)
+            ok, info = band_ok(got, ref, TOL)
+            say(f"  {variant} matrix {b}: rel_F {e:.3e}, band {info}")
+            assert e <= TOL and ok
+
+
+def test_k2_dense_3x7168x18432_structured(torch, ops):
+    n, m = 7168, 18432
+    say(f"case k2 dense 3x{n}x{m} with known SVD")
+    spec = np.arange(1, n + 1, dtype=np.float64) ** -0.5
+    rng = np.random.default_rng([3, 7])
+    facs, Gs = [], torch.empty(3, n, m, dtype=torch.bfloat16, device="cuda")
+    for b in range(3):
+        Ua = synth.orthonormal(rng, 56, 56); Ub = synth.orthonormal(rng, 128, 128)
+        Va = synth.orthonormal(rng, 144, 144); Vb = synth.orthonormal(rng, 128, 128)
+        Ut = torch.kron(torch.tensor(Ua, device="cuda"), torch.tensor(Ub, device="cuda")).float()
+        Vt = torch.kron(torch.tensor(Va, device="cuda"), torch.tensor(Vb, device="cuda"))[:, :n].float()
+        st = torch.tensor(spec, device="cuda").float()
+        Gs[b] = torch.matmul(Ut * st, Vt.t().contiguous()).to(torch.bfloat16)
+        del Ut, Vt
+        facs.append((Ua, Ub, Va, Vb))
+    torch.cuda.synchronize()
+    sel = np.random.default_rng(11)
+    rows = np.sort(sel.choice(n, 48, replace=False))
+    cols = np.sort(sel.choice(m, 48, replace=False))
+    for variant in ("gram_stabilized", "standard"):
+        O = ops.gram_ns(Gs) if variant != "standard" else ops.muon_ns(Gs)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(O.float()).all())
+        for b in range(3):
+            Ua, Ub, Va, Vb = facs[b]
+            Ur = np.stack([np.kron(Ua[i // 128], Ub[i % 128]) for i in rows])
+            Vr = np.stack([np.kron(Va[j // 128], Vb[j % 128])[:n] for j in cols])
+            nrm = float(torch.linalg.vector_norm(Gs[b].double()).item())
+            ref = oracle.ns_closed_form_entries(Ur, spec, Vr, fro_norm=nrm)
+            got = to_np(O[b][torch.tensor(rows, device="cuda")][:, torch.tensor(cols, device="cuda")])
+            e = rel_fro(got, ref)
+            say(f"  {variant} matrix {b}: sampled-entry rel_F {e:.3e}")
+            assert e <= TOL

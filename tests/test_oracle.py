@@ -286,3 +286,23 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert _closed_form_pin_fails(
         monkeypatch, "frobenius_normalize",
         lambda X, eps=1e-7: X / (np.linalg.norm(X, 2) + eps))
+
+
+def test_closed_form_entries_of_a_structured_input():
+    """Known-SVD inputs built from Kronecker products of small orthogonal factors (used for the
+    full-size checks): selected entries match the iteration run on the dense matrix."""
+    import synth
+    rng = np.random.default_rng(61)
+    n, m = 24, 60
+    spec = np.arange(1, n + 1) ** -0.5
+    G, (Ua, Ub, Va, Vb) = synth.structured_known_svd(rng, n, m, spec, na=4, ma=5)
+    U = np.kron(Ua, Ub)
+    V = np.kron(Va, Vb)[:, :n]
+    assert np.abs(U.T @ U - np.eye(n)).max() < 1e-12 and np.abs(V.T @ V - np.eye(n)).max() < 1e-12
+    full = oracle.ns_standard(G)
+    rows, cols = [0, 5, 23], [1, 17, 59]
+    blk = oracle.ns_closed_form_entries(U[rows], spec, V[cols])
+    assert np.abs(blk - full[np.ix_(rows, cols)]).max() < 1e-12
+    # with an explicit norm (the stored matrix's) as well
+    blk2 = oracle.ns_closed_form_entries(U[rows], spec, V[cols], fro_norm=np.linalg.norm(G))
+    assert np.abs(blk2 - blk).max() < 1e-12
