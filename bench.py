@@ -108,7 +108,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        k = 4
+        k = min(B, 24)          # bounded sample: the oracle stops after --cpu-budget seconds
         Gh = G[:k].double().cpu().numpy()
         Wh = W[:k].double().cpu().numpy()
 

@@ -100,6 +100,119 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
   if (tid == 0) p.partials[(int64_t)mat * p.tiles + blockIdx.x] = red[0];
 }
 
+
+// Vectorised prep for aligned buffers (ld, stride and base multiples of 8 elements / 16 B):
+// a 64 x 64 tile, each thread moves two 8-element vectors per direction. T is the input
+// dtype, which is also the internal dtype of the copies.
+template <typename T>
+__device__ inline void ld8(const T* p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t lo = (uint16_t)(w[e] & 0xffffu), hi = (uint16_t)(w[e] >> 16);
+      if constexpr (__is_same(T, __bf16)) { v[2 * e] = bf16_bits_to_f32(lo); v[2 * e + 1] = bf16_bits_to_f32(hi); }
+      else { v[2 * e] = f16_bits_to_f32(lo); v[2 * e + 1] = f16_bits_to_f32(hi); }
+    }
+  }
+}
+
+template <typename T>
+__device__ inline void st8(T* p, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t lo, hi;
+      if constexpr (__is_same(T, __bf16)) { lo = f32_to_bf16_bits(v[2 * e]); hi = f32_to_bf16_bits(v[2 * e + 1]); }
+      else { lo = f32_to_f16_bits(v[2 * e]); hi = f32_to_f16_bits(v[2 * e + 1]); }
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(p) = w;
+  }
+}
+
+template <typename T>
+__device__ inline float round_to(float v) {
+  if constexpr (__is_same(T, __bf16)) return bf16_bits_to_f32(f32_to_bf16_bits(v));
+  else if constexpr (__is_same(T, _Float16)) return f16_bits_to_f32(f32_to_f16_bits(v));
+  else return v;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) prep_vec_kernel(const PrepArgs p) {
+  __shared__ float tile[PREP_T][PREP_T + 4];
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  const int mat = blockIdx.y;
+  const int tx = blockIdx.x % p.tiles_x, ty = blockIdx.x / p.tiles_x;
+  const int r0 = ty * PREP_T, c0 = tx * PREP_T;
+  const T* Gb = reinterpret_cast<const T*>(p.G) + (int64_t)mat * p.sg;
+  float* Mb = p.M ? p.M + (int64_t)mat * p.sm : nullptr;
+  T* Sb = reinterpret_cast<T*>(p.out_same) + (int64_t)mat * p.s_same;
+  T* Tb = reinterpret_cast<T*>(p.out_tr) + (int64_t)mat * p.s_tr;
+  // thread -> rows (tid >> 3) and (tid >> 3) + 32, columns 8 (tid & 7) .. + 7
+  const int cv = (tid & 7) * 8;
+  double ss = 0.0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lr = (tid >> 3) + 32 * h, r = r0 + lr, c = c0 + cv;
+    float v[8];
+    if (r < p.rows && c < p.cols) {  // cols % 8 == 0: the vector is whole
+      const int64_t gi = (int64_t)r * p.ldg + c;
+      ld8<T>(Gb + gi, v);
+      if (Mb) {
+        const int64_t mi = (int64_t)r * p.ldm + c;
+        float m[8];
+        ld8<float>(Mb + mi, m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          m[e] = p.mu * m[e] + (1.f - p.mu) * v[e];
+          v[e] = p.nesterov ? p.mu * m[e] + (1.f - p.mu) * v[e] : m[e];
+        }
+        st8<float>(Mb + mi, m);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = round_to<T>(v[e]);
+        ss += (double)v[e] * (double)v[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    if (r < p.rows && c < p.ld_same) st8<T>(Sb + (int64_t)r * p.ld_same + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[lr][cv + e] = v[e];
+  }
+  __syncthreads();
+  // transposed: thread -> tile column (tid >> 3) and +32, rows 8 (tid & 7) .. + 7
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lc = (tid >> 3) + 32 * h, c = c0 + lc, r = r0 + cv;
+    if (c < p.cols && r < p.ld_tr) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[cv + e][lc];
+      st8<T>(Tb + (int64_t)c * p.ld_tr + r, v);
+    }
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) p.partials[(int64_t)mat * p.tiles + blockIdx.x] = red[0];
+}
+
 __global__ void __launch_bounds__(256) finalize_kernel(const double* partials, int tiles,
                                                        float eps, float* svec,
                                                        int32_t* flags) {

@@ -46,6 +46,9 @@ struct GemmArgs {
   int32_t* flags;
   // 1 when 8-element vectors of that buffer are aligned (ld, stride and base)
   int c_vec, ct_vec, w_vec, u_vec;
+  // nonzero: the typed fast epilogue applies (1: f16 out/f16 E, 2: bf16/bf16, 3: f16/bf16,
+  // 4: bf16/f16, 5: f32/f32)
+  int fast_epi;
 };
 
 template <typename T> struct MfmaTraits;
@@ -83,6 +86,9 @@ struct TileCfg {
 // Small problems: 128 x 128, 4 waves of 64 x 64, 128-byte k-stages, 2 waves per SIMD.
 // Large problems: 256 x 256, 16 waves of 64 x 64, 128-byte k-stages, 4 waves per SIMD
 // (one workgroup per CU; latency is hidden by the four waves each SIMD interleaves).
+#ifndef MNS_FRAG_DB
+#define MNS_FRAG_DB 0
+#endif
 #ifndef MNS_CFG128
 #define MNS_CFG128 128, 128, 2, 2, 128, 1, 2
 #endif
@@ -141,6 +147,46 @@ __device__ inline void store_part(void* p, int dt, int64_t idx, const float (&v)
   }
 }
 
+// Typed 8-element vector load/store (16-bit types: one 16-byte access; fp32: two).
+template <typename OT> struct VecIO;
+template <> struct VecIO<float> {
+  static __device__ inline void load(const void* p, int64_t idx, float (&v)[8]) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + idx);
+    const f32x4 a = q[0], b = q[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+  }
+  static __device__ inline void store(void* p, int64_t idx, const float (&v)[8]) {
+    f32x4* q = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + idx);
+    q[0] = f32x4{v[0], v[1], v[2], v[3]};
+    q[1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+};
+template <typename H> struct VecIO16 {
+  static __device__ inline float cvt(uint16_t h) {
+    if constexpr (__is_same(H, __bf16)) return bf16_bits_to_f32(h); else return f16_bits_to_f32(h);
+  }
+  static __device__ inline uint32_t bits(float f) {
+    if constexpr (__is_same(H, __bf16)) return f32_to_bf16_bits(f); else return f32_to_f16_bits(f);
+  }
+  static __device__ inline void load(const void* p, int64_t idx, float (&v)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p) + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = cvt((uint16_t)(w[e] & 0xffffu));
+      v[2 * e + 1] = cvt((uint16_t)(w[e] >> 16));
+    }
+  }
+  static __device__ inline void store(void* p, int64_t idx, const float (&v)[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = bits(v[2 * e]) | (bits(v[2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p) + idx) = w;
+  }
+};
+template <> struct VecIO<__bf16> : VecIO16<__bf16> {};
+template <> struct VecIO<_Float16> : VecIO16<_Float16> {};
+
 // MFMA operand fragment of one 32-row block for one 16-byte k-chunk group: 8 half values or
 // 4 fp32 values per lane (lane l holds row l % 32, chunk half l / 32 of the group).
 template <typename T> struct Frag { typedef T type __attribute__((ext_vector_type(8))); };
@@ -191,9 +237,115 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <typename T, bool TRI, class CFG>
+// Fast epilogue for internal outputs: C (row-major; mirrored for symmetric results) and
+// optionally C^T, both of dtype OT with rows padded to multiples of 8, E of dtype ET. No
+// runtime dtype dispatch and whole 16-byte vectors only.
+template <typename OT, typename ET, bool TRI, class CFG>
+__device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)[CFG::TM][CFG::TN],
+                                     int mat, int ti, int tj, int row0, int col0) {
+  constexpr int BN = CFG::BN, NT = CFG::NT, WTM = CFG::WTM, WTN = CFG::WTN, CP = CFG::CP;
+  constexpr int TM = CFG::TM, TN = CFG::TN, SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
+  float sc = 1.f;
+  if (p.spow) {
+    const float sb = p.svec[mat];
+    sc = p.spow == 1 ? sb : sb * sb;
+  }
+  constexpr int OS = sizeof(OT);
+  const char* Eb = p.E ? reinterpret_cast<const char*>(p.E) + (int64_t)mat * p.sE * sizeof(ET) : nullptr;
+  char* Cb = p.C ? reinterpret_cast<char*>(p.C) + (int64_t)mat * p.sC * OS : nullptr;
+  char* Ctb = p.Ct ? reinterpret_cast<char*>(p.Ct) + (int64_t)mat * p.sCt * OS : nullptr;
+  const bool diag = TRI && ti == tj;
+  const bool colpass = (TRI && Cb) || Ctb;
+  const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
+  float* Cs = reinterpret_cast<float*>(lds);
+  for (int sl = 0; sl < CFG::WVM / SR; ++sl) {
+    if (wm / SR == sl) {
+      const int lrow0 = (wm % SR) * WTM;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int r = lrow0 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            const int c = wn * WTN + j * 32 + (lane & 31);
+            Cs[r * CP + c] = acc[i][j][rr];
+          }
+    }
+    __syncthreads();
+    const int srow0 = row0 + sl * SROWS;
+    for (int idx = tid; idx < SROWS * VPR; idx += NT) {
+      const int lr = idx / VPR, lc = (idx - lr * VPR) * 8;
+      const int r = srow0 + lr, c = col0 + lc;
+      float* cs = Cs + lr * CP + lc;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(cs);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(cs + 4);
+      float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= c2;
+      if (Eb && r < p.e_rows && c < p.e_cols) {
+        float ev[8];
+        VecIO<ET>::load(Eb, (int64_t)r * p.lde + c, ev);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += c1 * ev[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] *= sc;
+        if (r == c + e && r < p.M) v[e] += c0;
+      }
+      if (colpass) {
+        *reinterpret_cast<f32x4*>(cs) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(cs + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
+      if (Cb && r < p.c_rows && c < p.c_cols) {
+        if (!diag || r <= c) {
+          VecIO<OT>::store(Cb, (int64_t)r * p.ldc + c, v);
+        } else if (r < c + 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e >= r) store_elem(Cb, sizeof(OT) == 4 ? F32 : (__is_same(OT, __bf16) ? BF16 : F16), (int64_t)r * p.ldc + c + e, v[e]);
+        }
+      }
+    }
+    if (colpass) {
+      __syncthreads();
+      for (int idx = tid; idx < BN * RVC; idx += NT) {
+        const int ci = idx & 15, ri = (idx >> 4) & 3, blk = idx >> 6;
+        const int cb = blk % (BN / 16), rb = blk / (BN / 16);
+        const int lc = cb * 16 + ci, lr = (rb * 4 + ri) * 8;
+        const int r = srow0 + lr, c = col0 + lc;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = Cs[(lr + e) * CP + lc];
+        if (TRI && Cb && c < p.c_rows && r < p.c_cols) {
+          if (!diag || r + 8 <= c) {
+            VecIO<OT>::store(Cb, (int64_t)c * p.ldc + r, v);
+          } else if (r < c) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (r + e < c) store_elem(Cb, sizeof(OT) == 4 ? F32 : (__is_same(OT, __bf16) ? BF16 : F16), (int64_t)c * p.ldc + r + e, v[e]);
+          }
+        }
+        if (Ctb && c < p.ct_rows && r < p.ct_cols) VecIO<OT>::store(Ctb, (int64_t)c * p.ldct + r, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// EPI selects the epilogue at compile time: 0 = generic (any dtypes, caller buffers, weight
+// update, flags); 1..5 = the typed fast epilogue (1: f16 out / f16 E, 2: bf16 / bf16,
+// 3: f16 / bf16, 4: bf16 / f16, 5: f32 / f32).
+// SHAPE: 0 = rectangular product, 1 = symmetric product of n x n iterates, 2 = Gram (X X^T);
+// 1 and 2 run the same code (triangle tiles) and differ only in the kernel symbol, so that
+// profiles separate the long-K Gram products from the n x n ones.
+template <typename T, int SHAPE, class CFG, int EPI>
 __global__ void __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::OCC, CFG::OCC)))
 gemm_nt_kernel(const GemmArgs p) {
+  constexpr bool TRI = SHAPE != 0;
   constexpr int ES = MfmaTraits<T>::ES;
   constexpr int EPC = 16 / ES;     // elements per 16-byte chunk
   constexpr int BK = CFG::CPR * EPC;  // elements of K per stage
@@ -204,7 +356,15 @@ gemm_nt_kernel(const GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
 
-  const int lid = xcd_remap(blockIdx.x, p.nblocks);
+  // Persistent: each workgroup walks a strided sequence of tiles inside its XCD's contiguous
+  // share of the tile list, so concurrently running tiles of one XCD are neighbours (same
+  // matrix, shared operand panels in that XCD's L2), and a tile's epilogue stores drain while
+  // the next tile's main loop runs.
+  constexpr int NXCD = 8;
+  const int xcd = blockIdx.x % NXCD, wgx = blockIdx.x / NXCD, per_xcd = gridDim.x / NXCD;
+  const int chunk = (p.nblocks + NXCD - 1) / NXCD;
+  const int t_begin = xcd * chunk, t_end = min(p.nblocks, t_begin + chunk);
+  for (int lid = t_begin + wgx; lid < t_end; lid += per_xcd) {
   const int mat = lid / p.tiles_per_mat;
   int t = lid - mat * p.tiles_per_mat;
   int ti, tj;
@@ -283,7 +443,7 @@ gemm_nt_kernel(const GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   typedef typename Frag<T>::type F;
-  F fa[2][TM], fb[2][TN];
+  F fa[MNS_FRAG_DB ? 2 : 1][TM], fb[MNS_FRAG_DB ? 2 : 1][TN];
   // Prologue: stage 0 in LDS, stages 1 .. PF-1 in flight in register sets 1 .. PF-1.
 #pragma unroll
   for (int s_ = 0; s_ < PF; ++s_)
@@ -302,11 +462,21 @@ gemm_nt_kernel(const GemmArgs p) {
     if (kt + PF < nk) load_stage((kt + PF) * BK, set);
     const char* As = lds + cur * CFG::STAGE + (wm * WTM) * ROWB;
     const char* Bs = lds + cur * CFG::STAGE + (BM + wn * WTN) * ROWB;
-    load_frags<T, TM, TN, ROWB>(As, Bs, lane, 0, fa[0], fb[0]);
+    if constexpr (MNS_FRAG_DB) {
+      // fragments of group g + 1 are read while group g's MFMAs run
+      load_frags<T, TM, TN, ROWB>(As, Bs, lane, 0, fa[0], fb[0]);
 #pragma unroll
-    for (int g = 0; g < CFG::NG; ++g) {
-      if (g + 1 < CFG::NG) load_frags<T, TM, TN, ROWB>(As, Bs, lane, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
-      mma<T, TM, TN>(fa[g & 1], fb[g & 1], acc);
+      for (int g = 0; g < CFG::NG; ++g) {
+        if (g + 1 < CFG::NG) load_frags<T, TM, TN, ROWB>(As, Bs, lane, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+        mma<T, TM, TN>(fa[g & 1], fb[g & 1], acc);
+      }
+    } else {
+      // one fragment set: the other waves of the SIMD cover the LDS latency
+#pragma unroll
+      for (int g = 0; g < CFG::NG; ++g) {
+        load_frags<T, TM, TN, ROWB>(As, Bs, lane, g, fa[0], fb[0]);
+        mma<T, TM, TN>(fa[0], fb[0], acc);
+      }
     }
     if (kt + 1 < nk) store_stage(cur ^ 1, nset);
     __syncthreads();
@@ -335,6 +505,14 @@ gemm_nt_kernel(const GemmArgs p) {
   }
 
   // ---------------------------------------------------------------- epilogue
+  if constexpr (EPI != 0) {
+    if constexpr (EPI == 1) epilogue_fast<_Float16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 2) epilogue_fast<__bf16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 3) epilogue_fast<_Float16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 4) epilogue_fast<__bf16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    else epilogue_fast<float, float, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    continue;
+  } else {
   // A) finish v = s^spow (c2 acc + c1 E) + c0 [i == j] in registers
   float sc = 1.f;
   if (p.spow) {
@@ -451,6 +629,9 @@ gemm_nt_kernel(const GemmArgs p) {
     __syncthreads();
   }
   if (p.flags && bad) atomicOr(p.flags + mat, 4);
+  break;  // the generic epilogue runs one tile per workgroup (no loop-carried state)
+  }  // generic epilogue
+  }  // tile loop
 }
 
 }  // namespace mns

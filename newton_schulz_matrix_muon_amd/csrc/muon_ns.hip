@@ -256,9 +256,49 @@ struct Prod {
   int32_t* flags = nullptr;
 };
 
+// Resident workgroups of a tile configuration on the current device (CUs x per-CU limit set
+// by LDS and waves), cached per device.
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+template <class CFG>
+int resident_slots() {
+  const int by_lds = (160 * 1024) / CFG::LDS;
+  const int by_waves = (4 * CFG::OCC) / (CFG::NT / 64);
+  const int per_cu = std::max(1, std::min(by_lds, by_waves));
+  return device_cus() * per_cu;
+}
+
 #ifndef MNS_GROUP_M
 #define MNS_GROUP_M 8
 #endif
+
+template <typename T, class CFG, int EPI>
+void launch_epi(int shape, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a) {
+  if (shape == 2) hipLaunchKernelGGL((gemm_nt_kernel<T, 2, CFG, EPI>), grid, block, 0, s, a);
+  else if (shape == 1) hipLaunchKernelGGL((gemm_nt_kernel<T, 1, CFG, EPI>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemm_nt_kernel<T, 0, CFG, EPI>), grid, block, 0, s, a);
+}
+
+template <typename T, class CFG>
+void launch_half(int shape, int epi, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a) {
+  switch (epi) {
+    case 1: launch_epi<T, CFG, 1>(shape, grid, block, s, a); break;
+    case 2: launch_epi<T, CFG, 2>(shape, grid, block, s, a); break;
+    case 3: launch_epi<T, CFG, 3>(shape, grid, block, s, a); break;
+    case 4: launch_epi<T, CFG, 4>(shape, grid, block, s, a); break;
+    default: launch_epi<T, CFG, 0>(shape, grid, block, s, a); break;
+  }
+}
 
 template <class CFG>
 int launch_prod(const Prod& q, GemmArgs a, int64_t batch, int kind, hipStream_t s) {
@@ -280,17 +320,20 @@ int launch_prod(const Prod& q, GemmArgs a, int64_t batch, int kind, hipStream_t 
   const int64_t nb = batch * (int64_t)a.tiles_per_mat;
   if (nb > INT32_MAX) return MNS_ERR_SHAPE;
   a.nblocks = (int)nb;
-  dim3 grid(a.nblocks), block(CFG::NT);
+  // persistent grid (typed fast epilogue): a multiple of the 8 XCDs, at most the resident
+  // workgroup slots; the generic epilogue runs one tile per workgroup
+  const int slots = a.fast_epi ? resident_slots<CFG>() : INT32_MAX;
+  const int g = (int)std::min<int64_t>(nb, slots);
+  dim3 grid(std::max(8, (g + 7) / 8 * 8)), block(CFG::NT);
+  const int shape = !q.tri ? 0 : (kind == K_SYRK ? 2 : 1);
   return launch(kind, s, [&] {
-    if (q.in_dt == BF16) {
-      if (q.tri) hipLaunchKernelGGL((gemm_nt_kernel<__bf16, true, CFG>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((gemm_nt_kernel<__bf16, false, CFG>), grid, block, 0, s, a);
-    } else if (q.in_dt == F16) {
-      if (q.tri) hipLaunchKernelGGL((gemm_nt_kernel<_Float16, true, CFG>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((gemm_nt_kernel<_Float16, false, CFG>), grid, block, 0, s, a);
+    if (q.in_dt == F32) {
+      if (a.fast_epi) launch_epi<float, CFG, 5>(shape, grid, block, s, a);
+      else launch_epi<float, CFG, 0>(shape, grid, block, s, a);
+    } else if (q.in_dt == BF16) {
+      launch_half<__bf16, CFG>(shape, a.fast_epi, grid, block, s, a);
     } else {
-      if (q.tri) hipLaunchKernelGGL((gemm_nt_kernel<float, true, CFG>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((gemm_nt_kernel<float, false, CFG>), grid, block, 0, s, a);
+      launch_half<_Float16, CFG>(shape, a.fast_epi, grid, block, s, a);
     }
   });
 }
@@ -329,6 +372,23 @@ int run_prod(const Prod& q, int64_t batch, int kind, hipStream_t s) {
   a.ct_vec = vec_ok(q.Ct, q.ldct, q.sCt);
   a.w_vec = vec_ok(q.W, q.ldw, q.sW);
   a.u_vec = vec_ok(q.U, q.ldu, q.sU);
+  // typed fast epilogue: internal outputs only (C, optional C^T of the same dtype, no weight
+  // update or flags), 8-aligned buffers and widths, E of a supported dtype pairing
+  a.fast_epi = 0;
+  {
+    const bool outs_ok = q.C && !q.W && !q.flags && a.c_vec && q.c_cols % 8 == 0 &&
+                         (!q.Ct || (a.ct_vec && q.ct_dt == q.c_dt && q.ct_cols % 8 == 0));
+    const int edt = q.E ? q.e_dt : q.c_dt;
+    const bool e_ok = !q.E || (q.lde % 8 == 0 && q.sE % 8 == 0 && q.e_cols % 8 == 0 &&
+                               reinterpret_cast<uintptr_t>(q.E) % 16 == 0);
+    if (outs_ok && e_ok) {
+      if (q.c_dt == F16 && edt == F16) a.fast_epi = 1;
+      else if (q.c_dt == BF16 && edt == BF16) a.fast_epi = 2;
+      else if (q.c_dt == F16 && edt == BF16) a.fast_epi = 3;
+      else if (q.c_dt == BF16 && edt == F16) a.fast_epi = 4;
+      else if (q.c_dt == F32 && edt == F32 && q.in_dt == F32) a.fast_epi = 5;
+    }
+  }
   switch (tile_choice(q, batch)) {
     case 1: return launch_prod<Tile256>(q, a, batch, kind, s);
     default: return launch_prod<Tile128>(q, a, batch, kind, s);
@@ -440,7 +500,19 @@ int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, 
     a.ldm = src.M->ld; a.sm = src.M->stride; a.mu = src.mu; a.nesterov = src.nesterov;
   }
   dim3 grid(g.prep_tiles, (unsigned)nb);
-  int st = launch(K_PREP, s, [&] { hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, s, a); });
+  // vectorised path: every row and the momentum buffer 16-byte aligned, widths multiples of 8
+  auto al = [](const void* ptr, int64_t ld, int64_t stride, int64_t batch) {
+    return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && ld % 8 == 0 && (batch == 1 || stride % 8 == 0);
+  };
+  const bool vec = G->dtype == c.io_dt && G->cols % 8 == 0 && G->rows % 8 == 0 &&
+                   al(G->ptr, G->ld, G->stride, G->batch) &&
+                   (!src.M || al(src.M->ptr, src.M->ld, src.M->stride, src.M->batch));
+  int st = launch(K_PREP, s, [&] {
+    if (!vec) hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, s, a);
+    else if (c.io_dt == BF16) hipLaunchKernelGGL(prep_vec_kernel<__bf16>, grid, dim3(256), 0, s, a);
+    else if (c.io_dt == F16) hipLaunchKernelGGL(prep_vec_kernel<_Float16>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(prep_vec_kernel<float>, grid, dim3(256), 0, s, a);
+  });
   if (st) return st;
   double* part = at<double>(ws, L.partials);
   float* sv = at<float>(ws, L.svec);

@@ -69,7 +69,8 @@ def test_expert_batch_1408x2048_muon_step(torch, ops, variant):
             assert ok, f"W update off at step {step}: {frac:.2e} of entries"
             # ... and the oracle's weights up to one bf16 step plus lr |U - U_oracle| (the
             # update's own deviation, bounded by the U check above)
-            ulp = np.spacing(np.abs(Wn).astype(np.float32)).astype(np.float64) * 2 ** 16
+            big = np.maximum(np.abs(Wn), np.abs(Wg)).astype(np.float32)
+            ulp = np.spacing(big).astype(np.float64) * 2 ** 16
             dev = np.abs(Wg - Wn) - lr * np.abs(Ug - Un)
             say(f"    W: {np.mean(bf16_steps(Wg, Wn) == 0):.4f} of entries equal to the oracle's rounded W")
             assert np.all(dev <= ulp + 1e-12)
