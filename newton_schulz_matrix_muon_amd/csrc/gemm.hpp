@@ -61,9 +61,14 @@ template <> struct MfmaTraits<float> { static constexpr int ES = 4; };
 // (KB = 128: 64 half / 32 fp32 values; KB = 64: half that). PF = number of k-stages whose
 // global loads are in flight in registers (1: the next stage, 2: the next two). OCC = waves
 // per SIMD the register budget is sized for.
-template <int BM_, int BN_, int WVM_, int WVN_, int KB_, int PF_, int OCC_>
+template <int BM_, int BN_, int WVM_, int WVN_, int KB_, int PF_, int OCC_, int NST_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WVM = WVM_, WVN = WVN_, KB = KB_, PF = PF_, OCC = OCC_;
+  // NST > 0: operands go global -> LDS by DMA (no register staging) into a ring of NST
+  // unpadded, XOR-swizzled k-stages, NST - 1 stages ahead of the one being consumed.
+  static constexpr int NST = NST_;
+  static constexpr bool DL = NST_ > 0;
+  static constexpr int STG = (BM_ + BN_) * KB_;          // bytes per DMA stage
   static constexpr int NT = 64 * WVM * WVN;
   static constexpr int WTM = BM / WVM, WTN = BN / WVN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -76,16 +81,19 @@ struct TileCfg {
   static constexpr int CP = BN + 4;
   static constexpr int SR = (WVM >= 4 && BM >= 256) ? 2 : 1;
   static constexpr int SLAB = SR * WTM * CP * 4;
-  static constexpr int LDS = 2 * STAGE > SLAB ? 2 * STAGE : SLAB;
+  static constexpr int MAINLDS = DL ? NST * STG : 2 * STAGE;
+  static constexpr int LDS = MAINLDS > SLAB ? MAINLDS : SLAB;
   static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile must be whole MFMA blocks");
   static_assert(CA * NT == BM * CPR && CB * NT == BN * CPR, "chunks must divide evenly");
   static_assert(NT % CPR == 0, "a thread keeps one chunk column");
   static_assert(WVM % SR == 0 && BN % 16 == 0 && (SR * WTM) % 32 == 0, "epilogue slab shape");
 };
 
-// Small problems: 128 x 128, 4 waves of 64 x 64, 128-byte k-stages, 2 waves per SIMD.
-// Large problems: 256 x 256, 16 waves of 64 x 64, 128-byte k-stages, 4 waves per SIMD
-// (one workgroup per CU; latency is hidden by the four waves each SIMD interleaves).
+// Small problems: 128 x 128, 4 waves of 64 x 64, 128-byte k-stages staged through registers,
+// 2 waves per SIMD.
+// Large problems: 256 x 256, 16 waves of 64 x 64, 128-byte k-stages DMA'd global -> LDS into a
+// 2-deep ring, 4 waves per SIMD (one workgroup per CU; latency is hidden by the four waves
+// each SIMD interleaves).
 #ifndef MNS_FRAG_DB
 #define MNS_FRAG_DB 0
 #endif
@@ -93,7 +101,7 @@ struct TileCfg {
 #define MNS_CFG128 128, 128, 2, 2, 128, 1, 2
 #endif
 #ifndef MNS_CFG256
-#define MNS_CFG256 256, 256, 4, 4, 128, 1, 4
+#define MNS_CFG256 256, 256, 4, 4, 128, 1, 4, 2
 #endif
 using Tile128 = TileCfg<MNS_CFG128>;
 using Tile256 = TileCfg<MNS_CFG256>;
@@ -204,6 +212,50 @@ __device__ inline void load_frags(const char* As, const char* Bs, int lane, int 
   for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * ROWB + off);
 }
 
+// XOR swizzle of the 16-byte chunk index within an unpadded k-stage row, as a function of the
+// row: conflict-free 16-byte fragment reads of 32 consecutive rows for 32- and 64-bank LDS.
+template <int CPR>
+__device__ __host__ constexpr int chunk_swizzle(int r) {
+  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+template <typename T, int TM, int TN, int KB>
+__device__ inline void load_frags_dl(const char* As, const char* Bs, int lane, int g, int sw,
+                                     typename Frag<T>::type (&a)[TM], typename Frag<T>::type (&b)[TN]) {
+  typedef typename Frag<T>::type F;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int off = (((2 * g + hi) ^ sw) << 4);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const F*>(As + (i * 32 + l32) * KB + off);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * KB + off);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt low/high bits, expcnt
+// and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Value known to be equal across the wave (kept in scalar registers).
+__device__ inline int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// 16-byte global -> LDS DMA of one lane; the wave's 64 lanes fill 1 KB at lds_base (uniform).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, char* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (LDS DMA completion is waited for explicitly);
+// the empty asm statements keep the compiler from moving memory operations across it.
+__device__ inline void barrier_nofence() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
 template <typename T, int TM, int TN>
 __device__ inline void mma(const typename Frag<T>::type (&a)[TM], const typename Frag<T>::type (&b)[TN],
                            f32x16 (&acc)[TM][TN]) {
@@ -235,6 +287,92 @@ __device__ inline void mma(const typename Frag<T>::type (&a)[TM], const typename
 constexpr uint32_t OOB = 0x80000000u;
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// scalar conversions and a 4-element (8- or 16-byte) store for the register-direct epilogue
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(__bf16 x) { return bf16_bits_to_f32(__builtin_bit_cast(uint16_t, x)); }
+__device__ inline float to_f32(_Float16 x) { return (float)x; }
+template <typename OT> __device__ inline OT from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline __bf16 from_f32<__bf16>(float x) { return __builtin_bit_cast(__bf16, f32_to_bf16_bits(x)); }
+template <> __device__ inline _Float16 from_f32<_Float16>(float x) { return __builtin_bit_cast(_Float16, f32_to_f16_bits(x)); }
+template <typename OT>
+__device__ inline void store4(OT* p, const float (&v)[4]) {
+  if constexpr (sizeof(OT) == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 w;
+    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[0])) | ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[1])) << 16);
+    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[2])) | ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[3])) << 16);
+    *reinterpret_cast<u32x2*>(p) = w;
+  }
+}
+
+// Register-direct epilogue for internal outputs (same conditions as the staged fast path):
+// each lane stores from the MFMA accumulator layout — lanes l and l + 32 hold 4 consecutive
+// rows of one column — so row-major stores are one element per lane (a 64-byte run per row
+// across 32 lanes) and transposed / mirrored stores are 4 consecutive elements per lane.
+// No LDS and no barriers.
+template <typename OT, typename ET, bool TRI, class CFG>
+__device__ inline void epilogue_direct(const GemmArgs& p, f32x16 (&acc)[CFG::TM][CFG::TN],
+                                       int mat, int ti, int tj, int row0, int col0) {
+  constexpr int TM = CFG::TM, TN = CFG::TN, WTM = CFG::WTM, WTN = CFG::WTN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
+  float sc = 1.f;
+  if (p.spow) {
+    const float sb = p.svec[mat];
+    sc = p.spow == 1 ? sb : sb * sb;
+  }
+  const ET* Eb = p.E ? reinterpret_cast<const ET*>(p.E) + (int64_t)mat * p.sE : nullptr;
+  OT* Cb = p.C ? reinterpret_cast<OT*>(p.C) + (int64_t)mat * p.sC : nullptr;
+  OT* Ctb = p.Ct ? reinterpret_cast<OT*>(p.Ct) + (int64_t)mat * p.sCt : nullptr;
+  const bool diag = TRI && ti == tj;
+  const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
+  const int cl = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = col0 + wn * WTN + j * 32 + cl;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rb = row0 + wm * WTM + i * 32 + 8 * q4 + 4 * hi;   // rows rb .. rb + 3
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb + e;
+          float x = c2 * acc[i][j][4 * q4 + e];
+          if (Eb && r < p.e_rows && c < p.e_cols) x += c1 * to_f32(Eb[(int64_t)r * p.lde + c]);
+          x *= sc;
+          if (r == c && r < p.M) x += c0;
+          v[e] = x;
+        }
+        if (Cb && c < p.c_cols) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rb + e;
+            if (r < p.c_rows && (!diag || r <= c)) Cb[(int64_t)r * p.ldc + c] = from_f32<OT>(v[e]);
+          }
+        }
+        // transposed destination (c, rb .. rb + 3): the mirror of a symmetric result, or C^T
+        OT* Tp = TRI ? Cb : Ctb;
+        const int trows = TRI ? p.c_rows : p.ct_rows, tcols = TRI ? p.c_cols : p.ct_cols;
+        const int64_t tld = TRI ? p.ldc : p.ldct;
+        if (Tp && c < trows && rb < tcols) {
+          const bool whole = rb + 4 <= tcols && (!diag || rb + 3 < c);
+          if (whole) {
+            store4<OT>(Tp + (int64_t)c * tld + rb, v);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (rb + e < tcols && (!diag || rb + e < c)) Tp[(int64_t)c * tld + rb + e] = from_f32<OT>(v[e]);
+          }
+        }
+      }
+    }
 }
 
 // Fast epilogue for internal outputs: C (row-major; mirrored for symmetric results) and
@@ -353,7 +491,8 @@ gemm_nt_kernel(const GemmArgs p) {
   constexpr int TM = CFG::TM, TN = CFG::TN, WTM = CFG::WTM, WTN = CFG::WTN, CP = CFG::CP;
   __shared__ __attribute__((aligned(16))) char lds[CFG::LDS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across a wave: keep it (and everything derived) in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
 
   // Persistent: each workgroup walks a strided sequence of tiles inside its XCD's contiguous
@@ -390,6 +529,82 @@ gemm_nt_kernel(const GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Ab, (uint32_t)((int64_t)p.M * p.lda * ES));
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bb, (uint32_t)((int64_t)p.N * p.ldb * ES));
 
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  if constexpr (CFG::DL) {
+    // ---- DMA main loop: global -> LDS without registers, NST-deep ring of k-stages
+    constexpr int KB = CFG::KB, CPR = CFG::CPR, NST = CFG::NST, PD = NST - 1;
+    constexpr int RPB = 1024 / KB;                 // rows per 1 KB DMA block (one wave instruction)
+    constexpr int NBA = BM / RPB, NBB = BN / RPB;
+    constexpr int NWAVE = NT / 64;
+    constexpr int D = (NBA + NBB) / NWAVE;         // DMA instructions per wave per stage
+    static_assert(D * NWAVE == NBA + NBB, "DMA blocks must divide over the waves");
+    static_assert(D * (PD > 0 ? PD : 1) < 64, "vmcnt range");
+    // per instruction j: LDS byte offset within a stage, operand, global byte offset (no k),
+    // and the chunk's k offset (elements)
+    uint32_t goff[D];
+    int kchunk[D];
+    int ldsoff[D];
+    bool isA[D];
+    const int rib = lane / CPR, pch = lane % CPR;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int blk = wave * D + j;
+      isA[j] = blk < NBA;
+      const int lrow = (isA[j] ? blk : blk - NBA) * RPB + rib;   // tile-local row
+      const int logical = pch ^ chunk_swizzle<CPR>(lrow);
+      const int grow = (isA[j] ? row0 : col0) + lrow;
+      const int lim = isA[j] ? p.M : p.N;
+      const int64_t ld = isA[j] ? p.lda : p.ldb;
+      goff[j] = grow < lim ? (uint32_t)(grow * ld * ES + logical * 16) : OOB;
+      kchunk[j] = logical * EPC;
+      ldsoff[j] = isA[j] ? blk * 1024 : BM * KB + (blk - NBA) * 1024;
+    }
+    const int nk = (p.K + BK - 1) / BK;
+    auto issue = [&](int ks) {
+      char* sb = lds + (ks % NST) * CFG::STG;
+      const int k0 = ks * BK;
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const uint32_t off = (k0 + kchunk[j] < p.K) ? goff[j] + (uint32_t)(k0 * ES) : OOB;
+        dma16(isA[j] ? rsA : rsB, sb + ldsoff[j], off);
+      }
+    };
+    // wait until at most m stages' DMAs (of this wave) are still in flight
+    auto wait_stages = [&](int m) {
+      if (m >= 3) wait_vmcnt<(3 * D < 64 ? 3 * D : 63)>();
+      else if (m == 2) wait_vmcnt<2 * D>();
+      else if (m == 1) wait_vmcnt<D>();
+      else wait_vmcnt<0>();
+    };
+    const int sw = chunk_swizzle<CPR>(lane & 31);
+    typedef typename Frag<T>::type F;
+    F fa[TM], fb[TN];
+#pragma unroll
+    for (int s_ = 0; s_ < PD; ++s_)
+      if (s_ < nk) issue(s_);
+    wait_stages(min(PD, nk) - 1);
+    barrier_nofence();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + PD < nk) issue(kt + PD);
+      const char* sb = lds + (kt % NST) * CFG::STG;
+      const char* As = sb + (wm * WTM) * KB;
+      const char* Bs = sb + (BM + wn * WTN) * KB;
+#pragma unroll
+      for (int g = 0; g < CFG::NG; ++g) {
+        load_frags_dl<T, TM, TN, KB>(As, Bs, lane, g, sw, fa, fb);
+        mma<T, TM, TN>(fa, fb, acc);
+      }
+      // stage kt + 1 must have landed; stages kt + 2 .. min(kt + PD, nk - 1) may be in flight
+      if (kt + 1 < nk) wait_stages(min(kt + PD, nk - 1) - (kt + 1));
+      barrier_nofence();
+    }
+  } else {
   // Global -> register staging, 16-byte chunks: chunk c = tid + NT q covers staged row
   // c / CPR, bytes 16 (c % CPR) .. +15. Row offsets are fixed per thread; rows past the end
   // get an out-of-range offset.
@@ -434,13 +649,6 @@ gemm_nt_kernel(const GemmArgs p) {
     }
   };
 
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   typedef typename Frag<T>::type F;
   F fa[MNS_FRAG_DB ? 2 : 1][TM], fb[MNS_FRAG_DB ? 2 : 1][TN];
@@ -504,8 +712,20 @@ gemm_nt_kernel(const GemmArgs p) {
     if (kt + 4 < nk) step(kt + 4, I0{}, I1{}, I2{});
   }
 
+  }  // register-staged main loop
+
   // ---------------------------------------------------------------- epilogue
-  if constexpr (EPI != 0) {
+#ifndef MNS_EPI_DIRECT
+#define MNS_EPI_DIRECT 0
+#endif
+  if constexpr (EPI != 0 && MNS_EPI_DIRECT) {
+    if constexpr (EPI == 1) epilogue_direct<_Float16, _Float16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 2) epilogue_direct<__bf16, __bf16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 3) epilogue_direct<_Float16, __bf16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 4) epilogue_direct<__bf16, _Float16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
+    else epilogue_direct<float, float, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
+    continue;
+  } else if constexpr (EPI != 0) {
     if constexpr (EPI == 1) epilogue_fast<_Float16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
     else if constexpr (EPI == 2) epilogue_fast<__bf16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
     else if constexpr (EPI == 3) epilogue_fast<_Float16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
