@@ -23,6 +23,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CSRC = os.path.join(ROOT, "newton_schulz_matrix_muon_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
@@ -36,12 +38,52 @@ def kind_work(kind: str, B: int, n: int, m: int):
         return B * flops.sym_flops(n, n), "flop", "mfma"
     if kind == "gemm_syrk":
         return B * flops.sym_flops(n, m), "flop", "mfma"
+    if kind == "gemm_square":
+        return B * 2 * n ** 3, "flop", "mfma"
     if kind == "gemm_rect":
         return B * flops.rect_flops(n, m), "flop", "mfma"
     if kind == "prep_norm":
         # read G (bf16) and M (fp32), write M (fp32) and the two bf16 copies of N
         return B * n * m * (2 + 4 + 4 + 2 + 2), "byte", "hbm"
     return None
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources (name + bytes, sorted): ties recorded counters to a build."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kind: str, workload: str):
+    """HBM bytes per launch of `kind` from the committed FETCH_SIZE / WRITE_SIZE summary of this
+    workload, or None when there is none or the kernels changed since it was taken."""
+    import glob
+    for path in glob.glob(os.path.join(PROFILES, "hbm_traffic_*.md")):
+        for line in open(path):
+            if not line.startswith("traffic-json: "):
+                continue
+            rec = json.loads(line[len("traffic-json: "):])
+            if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_digest():
+                continue
+            k = rec.get("kinds", {}).get(kind)
+            if k:
+                return k["bytes_per_launch"], os.path.basename(path)
+    return None, None
+
+
+def copy_probe(mib: int):
+    """A plain device copy of `mib` MiB (calibrates the HBM byte counters)."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(G_host, W_host, budget_s: float, variant: str):
@@ -80,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-standard", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -92,7 +136,11 @@ def main():
     from newton_schulz_matrix_muon_amd import flops, ops
 
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib > 0:
+        log(f"copy probe: {args.copy_probe_mib} MiB")
+        copy_probe(args.copy_probe_mib)
     B, r, c = args.batch, args.rows, args.cols
+    workload = f"kimi_k2_experts_{B}x{r}x{c}_bf16_gaussian_plus_rank32_spike"
     n, m = min(r, c), max(r, c)
     log(f"generating {B} x {r} x {c} bf16 gradients (Gaussian + rank-32 spike)")
     G = synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device=dev)
@@ -143,11 +191,15 @@ def main():
     def algo(variant):
         return flops.gram_flops(r, c) if variant == "gram" else flops.standard_flops(r, c)
 
+    def executed(variant):
+        return flops.gram_executed_flops(r, c) if variant == "gram" else flops.standard_flops(r, c)
+
     variants = {}
     def summarize(name, s):
         f = B * algo(name)
         variants[name] = {"ms_per_step": s * 1e3, "matrices_per_s": B / s,
-                          "executed_tflops": f / s / 1e12,
+                          "algorithmic_tflops": f / s / 1e12,
+                          "executed_tflops": B * executed(name) / s / 1e12,
                           "frac_bf16_peak": f / s / 1e12 / PEAK_MFMA_TFLOPS,
                           "std_equivalent_tflops": B * flops.standard_dense_flops(r, c) / s / 1e12}
     summarize(args.variant, sec)
@@ -173,6 +225,11 @@ def main():
         achieved = amount / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    traffic, tsrc = recorded_traffic(dom, workload)
+    roof["traffic"] = traffic
+    if traffic is not None:
+        roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roof["traffic_source"] = f"profiles/{tsrc}"
     roof["kernel"] = dom
     roof["avg_launch_ms"] = avg_s * 1e3
     roof["launches"] = launches
@@ -204,13 +261,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"kimi_k2_experts_{B}x{r}x{c}_bf16_gaussian_plus_rank32_spike",
+        "config": {"workload": workload,
                    "batch": B, "rows": r, "cols": c,
                    "step": f"fused Muon step, {args.variant} Newton-Schulz K=5"
                            + (" (fp16 iterates, restart after step 2)" if args.variant == "gram" else ""),
                    "lr": 0.02, "momentum": 0.95, "nesterov": True, "weight_decay": 0.01,
                    "scale": "0.2*sqrt(max(rows, cols))"},
-        "effective_tflops": variants[args.variant]["executed_tflops"],
+        "effective_tflops": variants[args.variant]["algorithmic_tflops"],
         "frac_bf16_peak": variants[args.variant]["frac_bf16_peak"],
         "ms_per_step_plain": sec_plain * 1e3,
         "variants": variants,

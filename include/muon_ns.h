@@ -149,6 +149,17 @@ int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
               const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
               void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
+/*
+ * Debug trace of the Gram iteration for the first matrix of G (diagnostics of the fp16
+ * instability the Gram Newton-Schulz article describes: negative eigenvalues of the Gram
+ * matrix). Runs gram_ns_batched on matrix 0 only and, after each step k = 1 .. K-1, copies the
+ * Gram iterate then in use (R_k = X_k X_k^T, re-formed at restarts) into trace[k-1] as fp32.
+ * trace: device float [K-1][n][n] row-major, n = min(rows, cols). O: as in gram_ns_batched
+ * (only matrix 0 is written). ws: workspace for a batch of one. Requires K >= 2.
+ */
+int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,
+                   size_t ws_bytes, float* trace, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* mns_status_string(int code);
 

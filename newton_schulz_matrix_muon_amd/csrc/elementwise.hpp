@@ -244,4 +244,14 @@ __global__ void __launch_bounds__(256) cast_kernel(const void* src, int s_dt, vo
     store_elem(db, d_dt, i, load_elem(sb, s_dt, i));
 }
 
+// rows x cols copy with dtype conversion between two strided 2-D buffers (diagnostics)
+__global__ void __launch_bounds__(256) copy2d_kernel(const void* src, int s_dt, int64_t lds_, void* dst,
+                                                     int d_dt, int64_t ldd, int rows, int cols) {
+  const int64_t n = (int64_t)rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols, c = i - r * cols;
+    store_elem(dst, d_dt, r * ldd + c, load_elem(src, s_dt, r * lds_ + c));
+  }
+}
+
 }  // namespace mns

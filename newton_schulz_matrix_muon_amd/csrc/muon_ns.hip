@@ -26,9 +26,9 @@ namespace {
 thread_local int g_last_hip = 0;
 
 // ------------------------------------------------------------------ launch timing
-enum Kind { K_PREP = 0, K_FINALIZE, K_SYRK, K_SYMPROD, K_RECT, K_CAST, NKINDS };
+enum Kind { K_PREP = 0, K_FINALIZE, K_SYRK, K_SYMPROD, K_RECT, K_CAST, K_SQUARE, NKINDS };
 const char* const kKindNames[NKINDS] = {"prep_norm", "finalize_norm", "gemm_syrk",
-                                        "gemm_symprod", "gemm_rect", "cast"};
+                                        "gemm_symprod", "gemm_rect", "cast", "gemm_square"};
 
 struct Timing {
   std::mutex mu;
@@ -439,6 +439,13 @@ Prod sym_prod(const void* A, const void* B, int in_dt, const Geo& g, void* C, in
   return q;
 }
 
+// Full n x n product C = A . B^T (no symmetry assumed: both triangles are computed).
+Prod square_prod(const void* A, const void* B, int in_dt, const Geo& g, void* C, int c_dt) {
+  Prod q = sym_prod(A, B, in_dt, g, C, c_dt);
+  q.tri = false;
+  return q;
+}
+
 // Gram product C = s^spow X X^T of the n x m row-major X.
 Prod gram_prod(const void* X, int io_dt, const Geo& g, void* C, int c_dt, const float* svec, int spow) {
   Prod q;
@@ -561,8 +568,20 @@ int run_standard(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64
   return MNS_OK;
 }
 
+// Copy the current Gram iterate of matrix 0 (n x ldn, iterate dtype) to trace (n x n fp32).
+int trace_copy(const char* R, int it, const Geo& g, float* dst, hipStream_t s) {
+  const int n = g.n;
+  const int64_t ldn = g.ldn;
+  const int64_t tot = (int64_t)n * n;
+  const int blocks = (int)std::min<int64_t>(4096, (tot + 255) / 256);
+  return launch(K_CAST, s, [&] {
+    hipLaunchKernelGGL(copy2d_kernel, dim3(blocks), dim3(256), 0, s, (const void*)R, it, ldn,
+                       (void*)dst, (int)F32, (int64_t)n, n, n);
+  });
+}
+
 int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b0, int64_t nb,
-             const FinalOut& fo, hipStream_t s) {
+             const FinalOut& fo, hipStream_t s, float* trace = nullptr) {
   const int io = c.io_dt, it = c.it_dt;
   const float* sv = at<float>(ws, L.svec);
   char* Xrow = at<char>(ws, L.X0);                       // n x ldm, overwritten at restarts
@@ -602,9 +621,15 @@ int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b
       qcur = 0;
       q_fresh = false;
     } else {
+      // Q <- Z Q as a full product, in the order the steps act on X (Q_k = Z_k ... Z_1). In
+      // rounded arithmetic the stored Z_j no longer commute exactly; keeping this ordered
+      // product, instead of forcing Q symmetric, halves the error the half-precision
+      // iterates add. Between updates the buffer holds Q^T, so both forms are NT products:
+      // Q^T_new = Q^T Z, and Q_new = Z (Q^T)^T when Q goes on to multiply X.
       const int nxt = qcur ^ 1;
-      q = sym_prod(Z, Qbuf[qcur], it, g, Qbuf[nxt], need_rect ? xdt : it);
-      if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+      q = need_rect ? square_prod(zdst, Qbuf[qcur], it, g, Qbuf[nxt], xdt)
+                    : square_prod(Qbuf[qcur], zdst, it, g, Qbuf[nxt], it);
+      if (int st = run_prod(q, nb, K_SQUARE, s)) return st;
       qcur = nxt;
     }
     if (restart) {
@@ -626,6 +651,9 @@ int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b
       q = sym_prod(zdst, Wb, it, g, R, it);
       if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
     }
+    if (trace && k < c.steps) {
+      if (int st = trace_copy(R, it, g, trace + (int64_t)(k - 1) * g.n * g.n, s)) return st;
+    }
   }
   // output = s^xspow Q X
   q = rect_prod(Qbuf[qcur], Xtb[xt], xdt, g);
@@ -635,7 +663,7 @@ int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b
 }
 
 int run_ns(int variant, const Source& src, const FinalOut& fo, const NsConf& c, void* ws,
-           size_t ws_bytes, int32_t* flags, hipStream_t s) {
+           size_t ws_bytes, int32_t* flags, hipStream_t s, float* trace = nullptr) {
   const Geo g = geometry(src.G);
   const int64_t batch = src.G->batch;
   const int64_t chunk = pick_chunk(variant, g, c, batch, ws_bytes);
@@ -647,7 +675,7 @@ int run_ns(int variant, const Source& src, const FinalOut& fo, const NsConf& c, 
     FinalOut f = fo;
     f.flags = flags;
     int st = variant == MNS_VARIANT_STANDARD ? run_standard(g, c, L, ws, b0, nb, f, s)
-                                             : run_gram(g, c, L, ws, b0, nb, f, s);
+                                             : run_gram(g, c, L, ws, b0, nb, f, s, trace);
     if (st) return st;
   }
   return MNS_OK;
@@ -732,6 +760,29 @@ int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, con
   fo.lr = sp->lr;
   fo.wd_mul = (float)(1.0 - (double)sp->lr * (double)sp->weight_decay);
   return run_ns(sp->variant, src, fo, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,
+                   size_t ws_bytes, float* trace, void* stream) {
+  if (int st = check_tensor(G)) return st;
+  if (int st = check_tensor(O)) return st;
+  if (!same_shape(G, O)) return MNS_ERR_SHAPE;
+  if (O->dtype != G->dtype) return MNS_ERR_DTYPE;
+  if (overlap(G, O)) return MNS_ERR_ARG;
+  if (!trace) return MNS_ERR_ARG;
+  NsConf c;
+  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (c.steps < 2) return MNS_ERR_ARG;
+  if (!ws) return MNS_ERR_WORKSPACE;
+  mns_tensor g1 = *G, o1 = *O;
+  g1.batch = 1;
+  o1.batch = 1;
+  Source src;
+  src.G = &g1;
+  FinalOut fo;
+  fo.O = &o1;
+  return run_ns(MNS_VARIANT_GRAM, src, fo, c, ws, ws_bytes, nullptr,
+                reinterpret_cast<hipStream_t>(stream), trace);
 }
 
 const char* mns_status_string(int code) {

@@ -68,6 +68,7 @@ def _lib():
             fn.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
         lib.muon_step.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
                                   P(MnsStepParams), P(MnsNsParams), vp, sz, vp, vp]
+        lib.gram_ns_trace.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
         lib.mns_status_string.argtypes = [ctypes.c_int]
         lib.mns_status_string.restype = ctypes.c_char_p
         lib.mns_last_hip_error.argtypes = []
@@ -78,7 +79,7 @@ def _lib():
         lib.mns_timing_kinds.argtypes = []
         lib.mns_kernel_kind_name.argtypes = [ctypes.c_int]
         lib.mns_kernel_kind_name.restype = ctypes.c_char_p
-        for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched,
+        for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched, lib.gram_ns_trace,
                   lib.muon_step, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
                   lib.mns_timing_reset, lib.mns_timing_query, lib.mns_timing_kinds):
             f.restype = ctypes.c_int
@@ -211,6 +212,24 @@ def muon_step(W, G, M, *, lr: float, momentum: float, weight_decay: float,
                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), fptr, _stream_ptr(G)),
            "muon_step")
     return W
+
+
+def gram_trace(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+               iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK):
+    """(O, trace) for the first matrix of G: the Gram iterate after each step 1 .. K-1 as a
+    [K-1, n, n] fp32 tensor (C ABI ``gram_ns_trace``)."""
+    torch = _torch()
+    G1 = G[0] if G.dim() == 3 else G
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G1), restart_mask)
+    n = min(G1.shape)
+    out = torch.empty_like(G1)
+    trace = torch.empty(steps - 1, n, n, dtype=torch.float32, device=G1.device)
+    ws = _workspace(GRAM, G1, p, None)
+    _check(_lib().gram_ns_trace(ctypes.byref(describe(G1)), ctypes.byref(describe(out)),
+                                 ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                 ctypes.c_void_p(trace.data_ptr()), _stream_ptr(G1)),
+           "gram_ns_trace")
+    return out, trace
 
 
 # ------------------------------------------------------------------ launch timing

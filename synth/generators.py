@@ -24,7 +24,7 @@ __all__ = [
     "Workload", "WORKLOADS", "host_rng", "orthonormal", "lowrank_plus_noise",
     "gaussian_plus_spike", "loguniform_spectrum", "stability_classes",
     "torch_lowrank_plus_noise", "torch_gaussian_plus_spike", "torch_weights",
-    "structured_known_svd",
+    "torch_loguniform_spectrum", "structured_known_svd",
 ]
 
 
@@ -139,12 +139,16 @@ def _tgen(device, workload_index: int, matrix_index: int):
 
 
 def _t_orthonormal(gen, batch, rows, cols, device):
+    """The Q factor (diag(R) > 0) of a Gaussian rows x cols matrix, by Cholesky QR applied
+    twice in fp64: Q = A R^-1 with R^T R = A^T A. Same factor as a Householder QR with the
+    signs fixed by diag(R), in a handful of batched launches."""
     torch = _torch()
     A = torch.randn(batch, rows, cols, generator=gen, device=device, dtype=torch.float32)
-    Q, R = torch.linalg.qr(A)
-    d = torch.sign(torch.diagonal(R, dim1=-2, dim2=-1))
-    d = torch.where(d == 0, torch.ones_like(d), d)
-    return Q * d.unsqueeze(-2)
+    A = A.to(torch.float64)
+    for _ in range(2):
+        L = torch.linalg.cholesky(A.transpose(-1, -2) @ A)
+        A = torch.linalg.solve_triangular(L, A.transpose(-1, -2), upper=False).transpose(-1, -2)
+    return A.to(torch.float32).contiguous()
 
 
 def torch_lowrank_plus_noise(batch: int, rows: int, cols: int, power: float, noise: float,
@@ -186,6 +190,26 @@ def torch_gaussian_plus_spike(batch: int, rows: int, cols: int, workload_index: 
         G = torch.randn(nb, rows, cols, generator=gen, device=device, dtype=torch.float32)
         G += sigma * torch.matmul(U, V.transpose(-1, -2).contiguous())
         out[b0:b0 + nb] = G.to(dtype)
+    return out
+
+
+def torch_loguniform_spectrum(batch: int, rows: int, cols: int, workload_index: int,
+                              seed_offset: int = 0, lo: float = 1e-6, hi: float = 1.0,
+                              device="cuda", chunk: int = 8):
+    """Device-side batch of U diag(s) V^T, s_j = exp(Uniform(ln lo, ln hi)) i.i.d. per matrix,
+    random orthonormal U (rows x r) and V (cols x r), r = min(rows, cols); fp32, no noise.
+    The caller rounds to the storage dtype."""
+    torch = _torch()
+    out = torch.empty(batch, rows, cols, device=device, dtype=torch.float32)
+    r = min(rows, cols)
+    for b0 in range(0, batch, chunk):
+        nb = min(chunk, batch - b0)
+        gen = _tgen(device, workload_index, seed_offset + b0)
+        U = _t_orthonormal(gen, nb, rows, r, device)
+        V = _t_orthonormal(gen, nb, cols, r, device)
+        u = torch.rand(nb, 1, r, generator=gen, device=device, dtype=torch.float64)
+        s = torch.exp(math.log(lo) + (math.log(hi) - math.log(lo)) * u).to(torch.float32)
+        out[b0:b0 + nb] = torch.matmul(U * s, V.transpose(-1, -2).contiguous())
     return out
 
 

@@ -113,6 +113,23 @@ def test_muon_step_argument_errors(L):
     assert f(s=ops.MnsStepParams(0.02, 0.95, 0.01, 0.2, 1, 5)) == -1
 
 
+def test_gram_trace_argument_errors(L):
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.F16)
+    G = _t(ops, ptr=0x10000, dtype=2)
+    O = _t(ops, ptr=0x90000000, dtype=2)
+    ws = ctypes.c_void_p(0x7f0000000000)
+    tr = ctypes.c_void_p(0x7e0000000000)
+    f = lambda g=G, pp=p, t=tr, wsp=ws, nb=1 << 40: L.gram_ns_trace(
+        ctypes.byref(g), ctypes.byref(O), ctypes.byref(pp), wsp, nb, t, None)
+    assert f(t=None) == -1                                             # no trace buffer
+    assert f(pp=ops.ns_params(steps=1, io_dtype=ops.F16)) == -1       # nothing to trace
+    assert f(wsp=None) == -4
+    assert f(nb=16) == -4
+    assert f(g=_t(ops, ptr=0x10000, dtype=1)) == -2                    # O dtype differs
+    assert L.mns_last_hip_error() == 0
+
+
 def test_timing_api_without_launches(L):
     from newton_schulz_matrix_muon_amd import ops
     names = [L.mns_kernel_kind_name(k).decode() for k in range(L.mns_timing_kinds())]

@@ -20,6 +20,12 @@ def test_dense_standard_count_is_the_articles_three_products():
 def test_gram_product_counts():
     assert flops.gram_products(5, ()) == (17, 1, 1)
     assert flops.gram_products(5, (2,)) == (14, 2, 2)
+    # executed: the Q updates (4 naive, 3 stabilized) are full products
+    assert flops.gram_products_executed(5, ()) == (13, 4, 1, 1)
+    assert flops.gram_products_executed(5, (2,)) == (11, 3, 2, 2)
+    n, m = 2048, 7168
+    extra = flops.gram_executed_flops(n, m) - flops.gram_flops(n, m)
+    assert extra == 3 * (2 * n ** 3 - n * (n + 1) * n)
 
 
 def test_reduction_range_against_the_article():

@@ -1,0 +1,214 @@
+"""Stability sweep of Gram Newton-Schulz in half precision (Gram NS article, sections on the
+fp16 instability of the naive Gram iteration and on the stabilized variant that restarts after
+step 2 and re-forms the Gram matrix).
+
+Inputs: 256 matrices G = U diag(s) V^T with s_j = exp(Uniform(ln 1e-6, 0)) i.i.d. and random
+orthonormal factors, no noise. Matrix i belongs to class c = i mod 12: n in {512, 1024, 2048}
+(c // 4) and n:m in {1:1, 1:2, 1:4, 1:8} (c % 4). Every matrix is stored once in fp16 and once
+in bf16. Runs: naive Gram (no restart), stabilized Gram (restart after step 2) and the
+standard iteration as a control, each with fp16 and with bf16 iterates; K = 5, quintic
+coefficients.
+
+Asserted
+  * the stabilized variant with fp16 iterates returns only finite values on all 256 matrices,
+    in both storage dtypes (the article's claim for its fix);
+  * bit 2 of the flags is set exactly for the matrices whose output holds a non-finite value;
+  * on the first matrix of each class (compared with the fp64 oracle on the exactly stored
+    input), the stabilized fp16-iterate run and the standard control meet the half-precision
+    bar: relative Frobenius error <= 2e-2 and every singular value inside the oracle's band.
+Reported (printed; written as JSON when MNS_REPORT_DIR is set)
+  * per class and run: matrices with non-finite output, relative Frobenius error and band of
+    the sampled matrix, and lambda_min(R_k) / lambda_max(R_k) of the Gram iterates the GPU
+    used after each step (fp64 eigenvalues of the traced fp16/bf16 matrices).
+
+The fp64 reference is the oracle's Gram iteration without restart: in fp64 the standard, naive
+and stabilized forms agree to ~1e-12 (pinned by the oracle tests, also on a log-uniform
+spectrum), so one reference serves every run.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import rel_fro, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+WORKLOAD = 4
+COUNT = 256
+
+
+def classes():
+    shapes = synth.stability_classes(COUNT)
+    out = []
+    for c in range(12):
+        idx = list(range(c, COUNT, 12))
+        out.append((c, shapes[c][0], shapes[c][1], len(idx)))
+    return out
+
+
+RUNS = [(v, it) for v in ("naive", "stabilized", "standard") for it in ("f16", "bf16")]
+REPORT = {"runs": {}, "sampled": {}, "eigen": {}}
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from newton_schulz_matrix_muon_amd import ops as o
+    o.lib()
+    return o
+
+
+def _run(ops, torch, G, variant, it):
+    itc = ops.F16 if it == "f16" else ops.BF16
+    flags = torch.zeros(G.shape[0], dtype=torch.int32, device=G.device)
+    if variant == "standard":
+        O = ops.muon_ns(G, iter_dtype=itc, flags=flags)
+    else:
+        mask = 0 if variant == "naive" else ops.STABILIZED_RESTART_MASK
+        O = ops.gram_ns(G, iter_dtype=itc, restart_mask=mask, flags=flags)
+    return O, flags
+
+
+@pytest.fixture(scope="module")
+def sweep(torch, ops):
+    """Every run on all 256 matrices; keeps the first matrix of each class (input and outputs)."""
+    stats = {}
+    samples = {}
+    for c, n, m, cnt in classes():
+        say(f"stability sweep: class {c} ({cnt} x {n} x {m})")
+        G32 = synth.torch_loguniform_spectrum(cnt, n, m, workload_index=WORKLOAD,
+                                              seed_offset=1000 * c, device="cuda", chunk=8)
+        for io in ("f16", "bf16"):
+            G = G32.to(torch.float16 if io == "f16" else torch.bfloat16)
+            samples[(c, io)] = {"G": G[0].cpu()}
+            for variant, it in RUNS:
+                O, flags = _run(ops, torch, G, variant, it)
+                finite = torch.isfinite(O).flatten(1).all(1)
+                torch.cuda.synchronize()
+                stats[(c, io, variant, it)] = {
+                    "nonfinite": int((~finite).sum()),
+                    "flag_mismatch": int(((flags & 4) != 0).ne(~finite).sum()),
+                    "flags_other": int(((flags & 3) != 0).sum()),
+                    "matrices": cnt}
+                samples[(c, io)][(variant, it)] = O[0].cpu()
+                del O
+            del G
+        del G32
+        torch.cuda.empty_cache()
+    for k, v in stats.items():
+        REPORT["runs"]["/".join(map(str, k))] = v
+    return stats, samples
+
+
+def test_stabilized_fp16_iterates_stay_finite(sweep):
+    stats, _ = sweep
+    bad = {k: v["nonfinite"] for k, v in stats.items()
+           if k[2] == "stabilized" and k[3] == "f16" and v["nonfinite"]}
+    for io in ("f16", "bf16"):
+        tot = sum(v["matrices"] for k, v in stats.items()
+                  if k[1] == io and k[2] == "stabilized" and k[3] == "f16")
+        assert tot == COUNT
+    summary = {}
+    for (c, io, variant, it), v in stats.items():
+        key = f"{variant}/{it} iterates, {io} storage"
+        summary[key] = summary.get(key, 0) + v["nonfinite"]
+    for k in sorted(summary):
+        say(f"  non-finite outputs, {k}: {summary[k]} of {COUNT}")
+    assert not bad, bad
+
+
+def test_flags_mark_exactly_the_non_finite_outputs(sweep):
+    stats, _ = sweep
+    assert all(v["flag_mismatch"] == 0 for v in stats.values())
+    assert all(v["flags_other"] == 0 for v in stats.values())   # finite, non-zero inputs
+
+
+def _band(O, lo, hi, tol):
+    s = np.sqrt(np.clip(np.linalg.eigvalsh(O @ O.T), 0.0, None))
+    return bool(s.min() >= lo - tol * hi and s.max() <= hi + tol * hi), float(s.min()), float(s.max())
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048])
+def test_sampled_matrices_against_the_oracle(sweep, n):
+    """rel_F for every run on the first matrix of each class; rel_F <= 2e-2 and the band for the
+    stabilized fp16-iterate run and the standard control."""
+    _, samples = sweep
+    fails = []
+    for c, nc, m, _ in classes():
+        if nc != n:
+            continue
+        for io in ("f16", "bf16"):
+            s = samples[(c, io)]
+            Gh = s["G"].double().numpy()
+            ref = oracle.ns_gram(Gh, restarts=())
+            sref = np.sqrt(np.clip(np.linalg.eigvalsh(ref @ ref.T), 0.0, None))
+            lo, hi = float(sref.min()), float(sref.max())
+            row = {}
+            for variant, it in RUNS:
+                O = s[(variant, it)].double().numpy()
+                fin = bool(np.isfinite(O).all())
+                r = rel_fro(O, ref) if fin else float("inf")
+                e = {"rel_fro": r}
+                if variant in ("stabilized", "standard") and it == "f16":
+                    ok, smin, smax = _band(O, lo, hi, TOL) if fin else (False, None, None)
+                    e.update(band_ok=ok, s_min=smin, s_max=smax, ref_lo=lo, ref_hi=hi)
+                    if not (fin and r <= TOL and ok):
+                        fails.append((c, io, variant, it, r, ok))
+                row[f"{variant}/{it}"] = e
+            REPORT["sampled"][f"{c}/{io}"] = row
+            say(f"  class {c:2d} {n}x{m} {io:4s}: " + "  ".join(
+                f"{k} {v['rel_fro']:.2e}" for k, v in row.items()))
+    assert not fails, fails
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048])
+def test_gram_iterate_eigenvalues(torch, ops, sweep, n):
+    """lambda_min / lambda_max of the GPU's Gram iterates after each step (fp16 storage),
+    naive vs stabilized, fp16 vs bf16 iterates. Reported; the finiteness bar is asserted above.
+    The traced iterates are exactly symmetric, and step 1 is the same for both variants."""
+    _, samples = sweep
+    for c, nc, m, _ in classes():
+        if nc != n:
+            continue
+        G = samples[(c, "f16")]["G"].to("cuda")
+        row = {}
+        first = {}
+        for variant in ("naive", "stabilized"):
+            for it in ("f16", "bf16"):
+                mask = 0 if variant == "naive" else ops.STABILIZED_RESTART_MASK
+                _, tr = ops.gram_trace(G, iter_dtype=ops.F16 if it == "f16" else ops.BF16,
+                                       restart_mask=mask)
+                trh = tr.double().cpu().numpy()
+                if it in first:
+                    assert np.array_equal(trh[0], first[it], equal_nan=True)
+                first[it] = trh[0]
+                ratios = []
+                for k in range(trh.shape[0]):
+                    R = trh[k]
+                    if not np.isfinite(R).all():
+                        ratios.append(None)
+                        continue
+                    assert np.array_equal(R, R.T)
+                    ev = np.linalg.eigvalsh(R)
+                    ratios.append(float(ev[0] / ev[-1]) if ev[-1] > 0 else None)
+                row[f"{variant}/{it}"] = ratios
+        REPORT["eigen"][str(c)] = row
+        say(f"  class {c:2d} {n}x{m}: " + "  ".join(
+            f"{k} " + ",".join("nan" if x is None else f"{x:.1e}" for x in v)
+            for k, v in row.items()))
+    out = os.environ.get("MNS_REPORT_DIR")
+    if out and n == 2048:
+        os.makedirs(out, exist_ok=True)
+        with open(os.path.join(out, "stability_sweep_256.json"), "w") as f:
+            json.dump(REPORT, f, indent=1)

@@ -187,6 +187,17 @@ def test_restart_set_does_not_change_the_exact_result():
         assert rel(oracle.ns_gram(G, eps=1e-7, restarts=rs), base) < 1e-12
 
 
+def test_all_forms_reach_the_closed_form_on_a_wide_log_uniform_spectrum():
+    """Singular values spread over six decades (the stability sweep's inputs): in fp64 the
+    standard, naive Gram and stabilized Gram iterations all equal U p^K(S) V^T."""
+    import synth
+    G = synth.loguniform_spectrum(synth.host_rng(4, 999), 96, 384)
+    ref = spectral_closed_form(G, eps=1e-7)
+    assert rel(oracle.ns_standard(G), ref) < 1e-11
+    assert rel(oracle.ns_gram(G, restarts=()), ref) < 1e-11
+    assert rel(oracle.ns_gram(G, restarts=(2,)), ref) < 1e-11
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_odd_scale_transpose_and_orthogonal_equivariance():
