@@ -31,21 +31,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kind_work(kind: str, B: int, n: int, m: int):
-    """Algorithmic work of one launch of a kernel kind: (amount, unit, bound)."""
+def kind_work(kind: str, groups):
+    """Algorithmic work of one launch of a kernel kind over the groups [(batch, n, m), ...]
+    (a launch covers every group): (amount, unit, bound)."""
     from newton_schulz_matrix_muon_amd import flops
-    if kind == "gemm_symprod":
-        return B * flops.sym_flops(n, n), "flop", "mfma"
-    if kind == "gemm_syrk":
-        return B * flops.sym_flops(n, m), "flop", "mfma"
-    if kind == "gemm_square":
-        return B * 2 * n ** 3, "flop", "mfma"
-    if kind == "gemm_rect":
-        return B * flops.rect_flops(n, m), "flop", "mfma"
-    if kind == "prep_norm":
-        # read G (bf16) and M (fp32), write M (fp32) and the two bf16 copies of N
-        return B * n * m * (2 + 4 + 4 + 2 + 2), "byte", "hbm"
-    return None
+    per = {"gemm_symprod": (lambda n, m: flops.sym_flops(n, n), "flop", "mfma"),
+           "gemm_square": (lambda n, m: 2 * n ** 3, "flop", "mfma"),
+           "gemm_syrk": (lambda n, m: flops.sym_flops(n, m), "flop", "mfma"),
+           "gemm_rect": (lambda n, m: flops.rect_flops(n, m), "flop", "mfma"),
+           # read G (bf16) and M (fp32), write M (fp32) and the two bf16 copies of N
+           "prep_norm": (lambda n, m: n * m * (2 + 4 + 4 + 2 + 2), "byte", "hbm")}
+    if kind not in per:
+        return None
+    f, unit, bound = per[kind]
+    return sum(B * f(n, m) for B, n, m in groups), unit, bound
 
 
 def kernel_source_digest() -> str:
@@ -116,6 +115,10 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--variant", choices=["gram", "standard"], default="gram")
+    ap.add_argument("--workload", choices=["experts", "k2_full"], default="experts",
+                    help="experts: one batch of --batch x --rows x --cols expert matrices (default "
+                         "648 x 2048 x 7168); k2_full: the whole Kimi-K2 step in one grouped call "
+                         "(432 x 2048 x 7168 up/gate, 216 x 7168 x 2048 down, 3 x 7168 x 18432 dense)")
     ap.add_argument("--batch", type=int, default=648)
     ap.add_argument("--rows", type=int, default=2048)
     ap.add_argument("--cols", type=int, default=7168)
@@ -127,8 +130,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; the batch dimension would shard "
-                          "across GPUs (see DESIGN.md), but --gpus > 1 is not supported"}))
+        print(json.dumps({"error": "--gpus > 1 is not supported: this library runs on one GPU (the "
+                          "batch of matrices would shard across GPUs with no exchange inside "
+                          "Newton-Schulz)"}))
         sys.exit(2)
 
     import torch
@@ -139,29 +143,43 @@ def main():
     if args.copy_probe_mib > 0:
         log(f"copy probe: {args.copy_probe_mib} MiB")
         copy_probe(args.copy_probe_mib)
-    B, r, c = args.batch, args.rows, args.cols
-    workload = f"kimi_k2_experts_{B}x{r}x{c}_bf16_gaussian_plus_rank32_spike"
-    n, m = min(r, c), max(r, c)
-    log(f"generating {B} x {r} x {c} bf16 gradients (Gaussian + rank-32 spike)")
-    G = synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device=dev)
-    W = synth.torch_weights(B, r, c, workload_index=2, device=dev)
-    M = torch.zeros(B, r, c, dtype=torch.float32, device=dev)
+    if args.workload == "experts":
+        shapes = [(args.batch, args.rows, args.cols)]
+        workload = f"kimi_k2_experts_{args.batch}x{args.rows}x{args.cols}_bf16_gaussian_plus_rank32_spike"
+    else:
+        shapes = [(432, 2048, 7168), (216, 7168, 2048), (3, 7168, 18432)]
+        workload = "kimi_k2_full_step_432x2048x7168+216x7168x2048+3x7168x18432_bf16_gaussian_plus_rank32_spike"
+    groups = [(B, min(r, c), max(r, c)) for B, r, c in shapes]
+    total = sum(B for B, _, _ in shapes)
+    Gs, Ws, Ms = [], [], []
+    for i, (B, r, c) in enumerate(shapes):
+        log(f"generating {B} x {r} x {c} bf16 gradients (Gaussian + rank-32 spike)")
+        Gs.append(synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device=dev))
+        Ws.append(synth.torch_weights(B, r, c, workload_index=2, device=dev, seed_offset=500_000 + i))
+        Ms.append(torch.zeros(B, r, c, dtype=torch.float32, device=dev))
     steps_kw = dict(lr=0.02, momentum=0.95, weight_decay=0.01, scale_coeff=0.2, nesterov=True)
 
     p_g = ops.ns_params(io_dtype=ops.BF16, restart_mask=1 << 2)
     p_s = ops.ns_params(io_dtype=ops.BF16, restart_mask=0)
-    ws_bytes = max(ops.workspace_bytes(ops.GRAM, G, p_g), ops.workspace_bytes(ops.STANDARD, G, p_s))
+    if len(shapes) == 1:
+        ws_bytes = max(ops.workspace_bytes(ops.GRAM, Gs[0], p_g), ops.workspace_bytes(ops.STANDARD, Gs[0], p_s))
+    else:
+        ws_bytes = max(ops.workspace_bytes_grouped(ops.GRAM, Gs, p_g),
+                       ops.workspace_bytes_grouped(ops.STANDARD, Gs, p_s))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     log(f"workspace {ws_bytes / 1e9:.1f} GB")
 
     cpu = None
     if not args.no_cpu_baseline:
-        k = min(B, 24)          # bounded sample: the oracle stops after --cpu-budget seconds
-        Gh = G[:k].double().cpu().numpy()
-        Wh = W[:k].double().cpu().numpy()
+        k = min(shapes[0][0], 24)     # bounded sample: the oracle stops after --cpu-budget seconds
+        Gh = Gs[0][:k].double().cpu().numpy()
+        Wh = Ws[0][:k].double().cpu().numpy()
 
     def step(variant_code):
-        ops.muon_step(W, G, M, variant=variant_code, workspace=ws, **steps_kw)
+        if len(shapes) == 1:
+            ops.muon_step(Ws[0], Gs[0], Ms[0], variant=variant_code, workspace=ws, **steps_kw)
+        else:
+            ops.muon_step_grouped(Ws, Gs, Ms, variant=variant_code, workspace=ws, **steps_kw)
 
     def timed(variant_code, steps, warmup, with_kernel_timing):
         for _ in range(warmup):
@@ -188,20 +206,23 @@ def main():
     sec_plain, _ = timed(main_code, max(1, args.steps // 2), 0, False)
     log(f"{args.variant}: {sec * 1e3:.2f} ms/step (with events), {sec_plain * 1e3:.2f} ms/step plain")
 
+    def work(fn):
+        return sum(B * fn(r, c) for B, r, c in shapes)
+
     def algo(variant):
-        return flops.gram_flops(r, c) if variant == "gram" else flops.standard_flops(r, c)
+        return work(flops.gram_flops if variant == "gram" else flops.standard_flops)
 
     def executed(variant):
-        return flops.gram_executed_flops(r, c) if variant == "gram" else flops.standard_flops(r, c)
+        return work(flops.gram_executed_flops if variant == "gram" else flops.standard_flops)
 
     variants = {}
     def summarize(name, s):
-        f = B * algo(name)
-        variants[name] = {"ms_per_step": s * 1e3, "matrices_per_s": B / s,
+        f = algo(name)
+        variants[name] = {"ms_per_step": s * 1e3, "matrices_per_s": total / s,
                           "algorithmic_tflops": f / s / 1e12,
-                          "executed_tflops": B * executed(name) / s / 1e12,
+                          "executed_tflops": executed(name) / s / 1e12,
                           "frac_bf16_peak": f / s / 1e12 / PEAK_MFMA_TFLOPS,
-                          "std_equivalent_tflops": B * flops.standard_dense_flops(r, c) / s / 1e12}
+                          "std_equivalent_tflops": work(flops.standard_dense_flops) / s / 1e12}
     summarize(args.variant, sec)
     if not args.skip_standard:
         other = "standard" if args.variant == "gram" else "gram"
@@ -216,7 +237,9 @@ def main():
     dom = max(kinds, key=lambda k: kinds[k][0])
     tot_ms, launches = kinds[dom]
     avg_s = tot_ms / launches / 1e3
-    amount, unit, bound = kind_work(dom, B, n, m)
+    amount, unit, bound = kind_work(dom, groups)
+    if dom in ("prep_norm", "finalize_norm"):   # one launch per group: average group's work
+        amount /= len(groups)
     if unit == "flop":
         achieved = amount / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
@@ -235,12 +258,14 @@ def main():
     roof["launches"] = launches
     per_kind = {}
     for k, (ms, cnt) in kinds.items():
-        w = kind_work(k, B, n, m)
+        w = kind_work(k, groups)
         e = {"total_ms_per_step": ms / args.steps, "launches_per_step": cnt / args.steps,
              "avg_launch_ms": ms / cnt}
         if w:
             amt, u, _ = w
-            e["achieved"] = amt / (ms / cnt / 1e3) / (1e12 if u == "flop" else 1e9)
+            # a GEMM launch covers every group; the norm kernels run once per group
+            rounds = cnt / args.steps / (len(groups) if k in ("prep_norm", "finalize_norm") else 1)
+            e["achieved"] = amt * rounds / (ms / args.steps / 1e3) / (1e12 if u == "flop" else 1e9)
             e["unit"] = "TFLOP/s" if u == "flop" else "GB/s"
         per_kind[k] = e
 
@@ -248,9 +273,17 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(Gh, Wh, args.cpu_budget, args.variant)
 
+    config = {"workload": workload,
+              "groups": [{"batch": B, "rows": r, "cols": c} for B, r, c in shapes],
+              "step": f"fused Muon step, {args.variant} Newton-Schulz K=5"
+                      + (" (fp16 iterates, restart after step 2)" if args.variant == "gram" else ""),
+              "lr": 0.02, "momentum": 0.95, "nesterov": True, "weight_decay": 0.01,
+              "scale": "0.2*sqrt(max(rows, cols))"}
+    if len(shapes) == 1:
+        config.update(batch=shapes[0][0], rows=shapes[0][1], cols=shapes[0][2])
     out = {
         "metric": "NS-orthogonalized matrices/sec and effective TFLOP/s (% bf16 MFMA peak)",
-        "value": B / sec,
+        "value": total / sec,
         "unit": "matrices/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -261,12 +294,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload,
-                   "batch": B, "rows": r, "cols": c,
-                   "step": f"fused Muon step, {args.variant} Newton-Schulz K=5"
-                           + (" (fp16 iterates, restart after step 2)" if args.variant == "gram" else ""),
-                   "lr": 0.02, "momentum": 0.95, "nesterov": True, "weight_decay": 0.01,
-                   "scale": "0.2*sqrt(max(rows, cols))"},
+        "config": config,
         "effective_tflops": variants[args.variant]["algorithmic_tflops"],
         "frac_bf16_peak": variants[args.variant]["frac_bf16_peak"],
         "ms_per_step_plain": sec_plain * 1e3,

@@ -150,6 +150,32 @@ int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
               void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
 /*
+ * Grouped calls: ngroups (1 .. 4) strided batches of different shapes in one call, e.g. the
+ * Kimi-K2 optimizer step of the Gram Newton-Schulz article's timing (expert up/gate matrices,
+ * expert down matrices in the transposed orientation, and the dense FFN matrices). Every group
+ * follows the conventions above on its own; all groups share one input dtype and one set of
+ * parameters. When the workspace holds every group at once (mns_workspace_bytes_grouped), each
+ * product step is a single launch over the tiles of all groups, so large groups' tail tiles
+ * share the chip with the other groups' tiles; otherwise the groups run one after another,
+ * each chunked as in the single-group calls. Results equal those of separate single-group
+ * calls bit for bit.
+ *  G, O, W, M, U_out: arrays of ngroups tensors (U_out may be NULL: no update output).
+ *  flags: device int32 [sum of the groups' batch sizes] or NULL; group g's matrices follow
+ *         those of groups 0 .. g-1.
+ *  Errors as for the single-group calls, plus MNS_ERR_ARG for ngroups outside 1 .. 4 or any
+ *  two output buffers (or an output and an input) that overlap.
+ */
+int mns_workspace_bytes_grouped(int variant, int ngroups, const mns_tensor* G,
+                                const mns_ns_params* p, size_t* bytes);
+int muon_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+                    void* ws, size_t ws_bytes, int32_t* flags, void* stream);
+int gram_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+                    void* ws, size_t ws_bytes, int32_t* flags, void* stream);
+int muon_step_grouped(int ngroups, const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
+                      const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
+                      void* ws, size_t ws_bytes, int32_t* flags, void* stream);
+
+/*
  * Debug trace of the Gram iteration for the first matrix of G (diagnostics of the fp16
  * instability the Gram Newton-Schulz article describes: negative eigenvalues of the Gram
  * matrix). Runs gram_ns_batched on matrix 0 only and, after each step k = 1 .. K-1, copies the

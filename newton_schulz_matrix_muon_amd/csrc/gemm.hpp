@@ -51,6 +51,19 @@ struct GemmArgs {
   int fast_epi;
 };
 
+// Several independent problems of one product kind in one launch (a grouped GEMM). Each
+// group's tile list (g[i].nblocks tiles) is cut into 8 equal parts, one per XCD, so every XCD
+// gets the same share of every group (balanced whatever the groups' tile costs) and keeps
+// neighbouring tiles of a group together (shared operand panels in its L2).
+#ifndef MNS_MAXG
+#define MNS_MAXG 4
+#endif
+struct GemmBatch {
+  GemmArgs g[MNS_MAXG];
+  int ng;
+};
+__host__ __device__ inline int xcd_part_lo(int nblocks, int x) { return (int)((int64_t)nblocks * x / 8); }
+
 template <typename T> struct MfmaTraits;
 template <> struct MfmaTraits<__bf16> { static constexpr int ES = 2; };
 template <> struct MfmaTraits<_Float16> { static constexpr int ES = 2; };
@@ -482,7 +495,7 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
 // profiles separate the long-K Gram products from the n x n ones.
 template <typename T, int SHAPE, class CFG, int EPI>
 __global__ void __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::OCC, CFG::OCC)))
-gemm_nt_kernel(const GemmArgs p) {
+gemm_nt_kernel(const GemmBatch gb) {
   constexpr bool TRI = SHAPE != 0;
   constexpr int ES = MfmaTraits<T>::ES;
   constexpr int EPC = 16 / ES;     // elements per 16-byte chunk
@@ -501,11 +514,21 @@ gemm_nt_kernel(const GemmArgs p) {
   // the next tile's main loop runs.
   constexpr int NXCD = 8;
   const int xcd = blockIdx.x % NXCD, wgx = blockIdx.x / NXCD, per_xcd = gridDim.x / NXCD;
-  const int chunk = (p.nblocks + NXCD - 1) / NXCD;
-  const int t_begin = xcd * chunk, t_end = min(p.nblocks, t_begin + chunk);
-  for (int lid = t_begin + wgx; lid < t_end; lid += per_xcd) {
-  const int mat = lid / p.tiles_per_mat;
-  int t = lid - mat * p.tiles_per_mat;
+  int xtiles = 0;  // this XCD's share: part xcd of every group, one group after another
+  for (int g = 0; g < gb.ng; ++g)
+    xtiles += xcd_part_lo(gb.g[g].nblocks, xcd + 1) - xcd_part_lo(gb.g[g].nblocks, xcd);
+  for (int j = wgx; j < xtiles; j += per_xcd) {
+  int gi = 0, jj = j;
+  for (;;) {
+    const int ps = xcd_part_lo(gb.g[gi].nblocks, xcd + 1) - xcd_part_lo(gb.g[gi].nblocks, xcd);
+    if (jj < ps || gi + 1 == gb.ng) break;
+    jj -= ps;
+    ++gi;
+  }
+  const GemmArgs& p = gb.g[gi];
+  const int glid = xcd_part_lo(p.nblocks, xcd) + jj;
+  const int mat = glid / p.tiles_per_mat;
+  int t = glid - mat * p.tiles_per_mat;
   int ti, tj;
   if constexpr (TRI) {
     const int nt = p.tiles_n;

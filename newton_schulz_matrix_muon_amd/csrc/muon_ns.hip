@@ -283,25 +283,26 @@ int resident_slots() {
 #endif
 
 template <typename T, class CFG, int EPI>
-void launch_epi(int shape, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a) {
-  if (shape == 2) hipLaunchKernelGGL((gemm_nt_kernel<T, 2, CFG, EPI>), grid, block, 0, s, a);
-  else if (shape == 1) hipLaunchKernelGGL((gemm_nt_kernel<T, 1, CFG, EPI>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemm_nt_kernel<T, 0, CFG, EPI>), grid, block, 0, s, a);
+void launch_epi(int shape, dim3 grid, dim3 block, hipStream_t s, const GemmBatch& b) {
+  if (shape == 2) hipLaunchKernelGGL((gemm_nt_kernel<T, 2, CFG, EPI>), grid, block, 0, s, b);
+  else if (shape == 1) hipLaunchKernelGGL((gemm_nt_kernel<T, 1, CFG, EPI>), grid, block, 0, s, b);
+  else hipLaunchKernelGGL((gemm_nt_kernel<T, 0, CFG, EPI>), grid, block, 0, s, b);
 }
 
 template <typename T, class CFG>
-void launch_half(int shape, int epi, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a) {
+void launch_half(int shape, int epi, dim3 grid, dim3 block, hipStream_t s, const GemmBatch& b) {
   switch (epi) {
-    case 1: launch_epi<T, CFG, 1>(shape, grid, block, s, a); break;
-    case 2: launch_epi<T, CFG, 2>(shape, grid, block, s, a); break;
-    case 3: launch_epi<T, CFG, 3>(shape, grid, block, s, a); break;
-    case 4: launch_epi<T, CFG, 4>(shape, grid, block, s, a); break;
-    default: launch_epi<T, CFG, 0>(shape, grid, block, s, a); break;
+    case 1: launch_epi<T, CFG, 1>(shape, grid, block, s, b); break;
+    case 2: launch_epi<T, CFG, 2>(shape, grid, block, s, b); break;
+    case 3: launch_epi<T, CFG, 3>(shape, grid, block, s, b); break;
+    case 4: launch_epi<T, CFG, 4>(shape, grid, block, s, b); break;
+    default: launch_epi<T, CFG, 0>(shape, grid, block, s, b); break;
   }
 }
 
+// Tile counts of one group's product for tile shape CFG.
 template <class CFG>
-int launch_prod(const Prod& q, GemmArgs a, int64_t batch, int kind, hipStream_t s) {
+int set_tiles(const Prod& q, GemmArgs& a, int64_t batch) {
   const int cover_n = std::max({q.N, q.C ? q.c_cols : 0, q.Ct ? q.ct_rows : 0});
   const int cover_m = std::max({q.M, q.C ? q.c_rows : 0, q.Ct ? q.ct_cols : 0});
   const int tm = (cover_m + CFG::BM - 1) / CFG::BM;
@@ -320,20 +321,42 @@ int launch_prod(const Prod& q, GemmArgs a, int64_t batch, int kind, hipStream_t 
   const int64_t nb = batch * (int64_t)a.tiles_per_mat;
   if (nb > INT32_MAX) return MNS_ERR_SHAPE;
   a.nblocks = (int)nb;
-  // persistent grid (typed fast epilogue): a multiple of the 8 XCDs, at most the resident
-  // workgroup slots; the generic epilogue runs one tile per workgroup
-  const int slots = a.fast_epi ? resident_slots<CFG>() : INT32_MAX;
-  const int g = (int)std::min<int64_t>(nb, slots);
-  dim3 grid(std::max(8, (g + 7) / 8 * 8)), block(CFG::NT);
-  const int shape = !q.tri ? 0 : (kind == K_SYRK ? 2 : 1);
+  return MNS_OK;
+}
+
+// One launch over ng groups that share the kernel instantiation (dtype, shape kind, epilogue).
+template <class CFG>
+int launch_prod(const Prod* qs, const GemmArgs* as, const int64_t* batches, int ng, int kind, hipStream_t s) {
+  GemmBatch b;
+  for (int i = 0; i < ng; ++i) {
+    b.g[i] = as[i];
+    if (int st = set_tiles<CFG>(qs[i], b.g[i], batches[i])) return st;
+  }
+  b.ng = ng;
+  // tiles of the busiest XCD (each XCD takes part x of every group)
+  int64_t xmax = 0;
+  for (int x = 0; x < 8; ++x) {
+    int64_t t = 0;
+    for (int i = 0; i < ng; ++i) t += xcd_part_lo(b.g[i].nblocks, x + 1) - xcd_part_lo(b.g[i].nblocks, x);
+    xmax = std::max(xmax, t);
+  }
+  if (8 * xmax > INT32_MAX) return MNS_ERR_SHAPE;
+  // persistent grid (typed fast epilogue): 8 x (workgroups per XCD), at most the resident
+  // workgroup slots; the generic epilogue runs one tile per workgroup, so its grid covers the
+  // busiest XCD's share
+  const int fast = as[0].fast_epi;
+  const int64_t per_xcd = fast ? std::min<int64_t>(xmax, std::max(1, resident_slots<CFG>() / 8)) : xmax;
+  dim3 grid((unsigned)(8 * std::max<int64_t>(1, per_xcd))), block(CFG::NT);
+  const int shape = !qs[0].tri ? 0 : (kind == K_SYRK ? 2 : 1);
+  const int in_dt = qs[0].in_dt;
   return launch(kind, s, [&] {
-    if (q.in_dt == F32) {
-      if (a.fast_epi) launch_epi<float, CFG, 5>(shape, grid, block, s, a);
-      else launch_epi<float, CFG, 0>(shape, grid, block, s, a);
-    } else if (q.in_dt == BF16) {
-      launch_half<__bf16, CFG>(shape, a.fast_epi, grid, block, s, a);
+    if (in_dt == F32) {
+      if (fast) launch_epi<float, CFG, 5>(shape, grid, block, s, b);
+      else launch_epi<float, CFG, 0>(shape, grid, block, s, b);
+    } else if (in_dt == BF16) {
+      launch_half<__bf16, CFG>(shape, fast, grid, block, s, b);
     } else {
-      launch_half<_Float16, CFG>(shape, a.fast_epi, grid, block, s, a);
+      launch_half<_Float16, CFG>(shape, fast, grid, block, s, b);
     }
   });
 }
@@ -350,7 +373,7 @@ int tile_choice(const Prod& q, int64_t batch) {
   return MNS_TILE_POLICY;
 }
 
-int run_prod(const Prod& q, int64_t batch, int kind, hipStream_t s) {
+GemmArgs gemm_args(const Prod& q, int64_t batch) {
   GemmArgs a;
   a.A = q.A; a.lda = q.lda; a.sA = q.sA;
   a.B = q.B; a.ldb = q.ldb; a.sB = q.sB;
@@ -364,6 +387,7 @@ int run_prod(const Prod& q, int64_t batch, int kind, hipStream_t s) {
   a.U = q.U; a.u_dt = q.u_dt; a.ldu = q.ldu; a.sU = q.sU;
   a.u_scale = q.u_scale; a.lr = q.lr; a.wd_mul = q.wd_mul;
   a.flags = q.flags;
+  a.tiles_m = a.tiles_n = a.tiles_per_mat = a.nblocks = a.group_m = 0;
   auto vec_ok = [&](const void* ptr, int64_t ld, int64_t stride) {
     return (int)(ptr && ld % 8 == 0 && (batch == 1 || stride % 8 == 0) &&
                  reinterpret_cast<uintptr_t>(ptr) % 16 == 0);
@@ -375,25 +399,47 @@ int run_prod(const Prod& q, int64_t batch, int kind, hipStream_t s) {
   // typed fast epilogue: internal outputs only (C, optional C^T of the same dtype, no weight
   // update or flags), 8-aligned buffers and widths, E of a supported dtype pairing
   a.fast_epi = 0;
-  {
-    const bool outs_ok = q.C && !q.W && !q.flags && a.c_vec && q.c_cols % 8 == 0 &&
-                         (!q.Ct || (a.ct_vec && q.ct_dt == q.c_dt && q.ct_cols % 8 == 0));
-    const int edt = q.E ? q.e_dt : q.c_dt;
-    const bool e_ok = !q.E || (q.lde % 8 == 0 && q.sE % 8 == 0 && q.e_cols % 8 == 0 &&
-                               reinterpret_cast<uintptr_t>(q.E) % 16 == 0);
-    if (outs_ok && e_ok) {
-      if (q.c_dt == F16 && edt == F16) a.fast_epi = 1;
-      else if (q.c_dt == BF16 && edt == BF16) a.fast_epi = 2;
-      else if (q.c_dt == F16 && edt == BF16) a.fast_epi = 3;
-      else if (q.c_dt == BF16 && edt == F16) a.fast_epi = 4;
-      else if (q.c_dt == F32 && edt == F32 && q.in_dt == F32) a.fast_epi = 5;
-    }
+  const bool outs_ok = q.C && !q.W && !q.flags && a.c_vec && q.c_cols % 8 == 0 &&
+                       (!q.Ct || (a.ct_vec && q.ct_dt == q.c_dt && q.ct_cols % 8 == 0));
+  const int edt = q.E ? q.e_dt : q.c_dt;
+  const bool e_ok = !q.E || (q.lde % 8 == 0 && q.sE % 8 == 0 && q.e_cols % 8 == 0 &&
+                             reinterpret_cast<uintptr_t>(q.E) % 16 == 0);
+  if (outs_ok && e_ok) {
+    if (q.c_dt == F16 && edt == F16) a.fast_epi = 1;
+    else if (q.c_dt == BF16 && edt == BF16) a.fast_epi = 2;
+    else if (q.c_dt == F16 && edt == BF16) a.fast_epi = 3;
+    else if (q.c_dt == BF16 && edt == F16) a.fast_epi = 4;
+    else if (q.c_dt == F32 && edt == F32 && q.in_dt == F32) a.fast_epi = 5;
   }
-  switch (tile_choice(q, batch)) {
-    case 1: return launch_prod<Tile256>(q, a, batch, kind, s);
-    default: return launch_prod<Tile128>(q, a, batch, kind, s);
+  return a;
+}
+
+// One product kind over ng groups (each a strided batch of its own shape): one launch when the
+// groups agree on the kernel instantiation and tile shape, else one launch per group.
+int run_prods(const Prod* qs, const int64_t* batches, int ng, int kind, hipStream_t s) {
+  if (ng < 1 || ng > MNS_MAXG) return MNS_ERR_ARG;
+  GemmArgs as[MNS_MAXG];
+  int tc[MNS_MAXG];
+  bool same = true;
+  for (int i = 0; i < ng; ++i) {
+    as[i] = gemm_args(qs[i], batches[i]);
+    tc[i] = tile_choice(qs[i], batches[i]);
+    if (i && (qs[i].in_dt != qs[0].in_dt || qs[i].tri != qs[0].tri ||
+              as[i].fast_epi != as[0].fast_epi || tc[i] != tc[0]))
+      same = false;
+  }
+  if (!same) {
+    for (int i = 0; i < ng; ++i)
+      if (int st = run_prods(qs + i, batches + i, 1, kind, s)) return st;
+    return MNS_OK;
+  }
+  switch (tc[0]) {
+    case 1: return launch_prod<Tile256>(qs, as, batches, ng, kind, s);
+    default: return launch_prod<Tile128>(qs, as, batches, ng, kind, s);
   }
 }
+
+int run_prod(const Prod& q, int64_t batch, int kind, hipStream_t s) { return run_prods(&q, &batch, 1, kind, s); }
 
 // Final destination of the last rectangular product.
 struct FinalOut {
@@ -531,14 +577,38 @@ int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, 
   });
 }
 
-int run_standard(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b0, int64_t nb,
-                 const FinalOut& fo, hipStream_t s) {
+// One group's share of a call: its geometry, workspace layout and base, the batch chunk
+// [b0, b0 + nb) being processed, and where its results go.
+struct Part {
+  Geo g;
+  Layout L;
+  char* ws = nullptr;
+  int64_t b0 = 0, nb = 0;
+  Source src;
+  FinalOut fo;
+};
+
+// Run one product kind over all parts: make(i) builds part i's product.
+template <class F>
+int run_all(const Part* P, int np, int kind, hipStream_t s, F&& make) {
+  Prod qs[MNS_MAXG];
+  int64_t nbs[MNS_MAXG];
+  for (int i = 0; i < np; ++i) {
+    qs[i] = make(i);
+    nbs[i] = P[i].nb;
+  }
+  return run_prods(qs, nbs, np, kind, s);
+}
+
+int run_standard(const Part* P, int np, const NsConf& c, hipStream_t s) {
   const int io = c.io_dt, it = c.it_dt;
-  const float* sv = at<float>(ws, L.svec);
-  char* X[2] = {at<char>(ws, L.X0), at<char>(ws, L.X1)};
-  char* Xt[2] = {at<char>(ws, L.Xt0), at<char>(ws, L.Xt1)};
-  char* A = at<char>(ws, L.A);
-  char* Bm = at<char>(ws, L.Bm);
+  struct Bufs { const float* sv; char* X[2]; char* Xt[2]; char* A; char* Bm; } B[MNS_MAXG];
+  for (int i = 0; i < np; ++i) {
+    const Layout& L = P[i].L;
+    void* ws = P[i].ws;
+    B[i] = {at<float>(ws, L.svec), {at<char>(ws, L.X0), at<char>(ws, L.X1)},
+            {at<char>(ws, L.Xt0), at<char>(ws, L.Xt1)}, at<char>(ws, L.A), at<char>(ws, L.Bm)};
+  }
   int cur = 0;
   // X0 is the caller's values in the input dtype; every later X_k is normalised and is
   // stored in the iterate dtype (fp16 keeps 3 more mantissa bits than bf16 for B X).
@@ -547,21 +617,30 @@ int run_standard(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64
     const float a_k = c.coeff[k - 1][0], b_k = c.coeff[k - 1][1], c_k = c.coeff[k - 1][2];
     const bool first = k == 1;
     // A = X X^T (scaled by s^2 on the unnormalised first iterate)
-    Prod q = gram_prod(X[cur], xdt, g, A, it, sv, first ? 2 : 0);
-    if (int st = run_prod(q, nb, K_SYRK, s)) return st;
+    if (int st = run_all(P, np, K_SYRK, s, [&](int i) {
+          return gram_prod(B[i].X[cur], xdt, P[i].g, B[i].A, it, B[i].sv, first ? 2 : 0);
+        })) return st;
     // B = b A + c A^2, stored in the dtype of X (the two are the operands of B X)
-    q = sym_prod(A, A, it, g, Bm, xdt);
-    q.c0 = 0.f; q.c1 = b_k; q.c2 = c_k;
-    q.E = A; q.e_dt = it; q.lde = g.ldn; q.sE = (int64_t)g.n * g.ldn; q.e_rows = g.n; q.e_cols = (int)g.ldn;
-    if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+    if (int st = run_all(P, np, K_SYMPROD, s, [&](int i) {
+          const Geo& g = P[i].g;
+          Prod q = sym_prod(B[i].A, B[i].A, it, g, B[i].Bm, xdt);
+          q.c0 = 0.f; q.c1 = b_k; q.c2 = c_k;
+          q.E = B[i].A; q.e_dt = it; q.lde = g.ldn; q.sE = (int64_t)g.n * g.ldn; q.e_rows = g.n;
+          q.e_cols = (int)g.ldn;
+          return q;
+        })) return st;
     // X <- s (a X + B X)
-    q = rect_prod(Bm, Xt[cur], xdt, g);
-    q.svec = sv; q.spow = first ? 1 : 0;
-    q.c1 = a_k; q.c2 = 1.f;
-    q.E = X[cur]; q.e_dt = xdt; q.lde = g.ldm; q.sE = (int64_t)g.n * g.ldm; q.e_rows = g.n; q.e_cols = (int)g.ldm;
-    if (k < c.steps) set_internal_x_out(q, X[cur ^ 1], Xt[cur ^ 1], it, g);
-    else set_final(q, fo, g, b0);
-    if (int st = run_prod(q, nb, K_RECT, s)) return st;
+    if (int st = run_all(P, np, K_RECT, s, [&](int i) {
+          const Geo& g = P[i].g;
+          Prod q = rect_prod(B[i].Bm, B[i].Xt[cur], xdt, g);
+          q.svec = B[i].sv; q.spow = first ? 1 : 0;
+          q.c1 = a_k; q.c2 = 1.f;
+          q.E = B[i].X[cur]; q.e_dt = xdt; q.lde = g.ldm; q.sE = (int64_t)g.n * g.ldm; q.e_rows = g.n;
+          q.e_cols = (int)g.ldm;
+          if (k < c.steps) set_internal_x_out(q, B[i].X[cur ^ 1], B[i].Xt[cur ^ 1], it, g);
+          else set_final(q, P[i].fo, g, P[i].b0);
+          return q;
+        })) return st;
     cur ^= 1;
     xdt = it;
   }
@@ -580,23 +659,24 @@ int trace_copy(const char* R, int it, const Geo& g, float* dst, hipStream_t s) {
   });
 }
 
-int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b0, int64_t nb,
-             const FinalOut& fo, hipStream_t s, float* trace = nullptr) {
+int run_gram(const Part* P, int np, const NsConf& c, hipStream_t s, float* trace = nullptr) {
   const int io = c.io_dt, it = c.it_dt;
-  const float* sv = at<float>(ws, L.svec);
-  char* Xrow = at<char>(ws, L.X0);                       // n x ldm, overwritten at restarts
-  char* Xtb[2] = {at<char>(ws, L.Xt0), L.Xt1.per ? at<char>(ws, L.Xt1) : nullptr};
+  struct Bufs { const float* sv; char* Xrow; char* Xtb[2]; char* R; char* Z; char* Wb; char* Qbuf[2]; } B[MNS_MAXG];
+  for (int i = 0; i < np; ++i) {
+    const Layout& L = P[i].L;
+    void* ws = P[i].ws;
+    B[i] = {at<float>(ws, L.svec), at<char>(ws, L.X0),            // X: n x ldm, overwritten at restarts
+            {at<char>(ws, L.Xt0), L.Xt1.per ? at<char>(ws, L.Xt1) : nullptr},
+            at<char>(ws, L.R), at<char>(ws, L.Z), at<char>(ws, L.W),
+            {at<char>(ws, L.Qa), at<char>(ws, L.Qb)}};
+  }
   int xt = 0;
-  char* R = at<char>(ws, L.R);
-  char* Z = at<char>(ws, L.Z);
-  char* Wb = at<char>(ws, L.W);
-  char* Qbuf[2] = {at<char>(ws, L.Qa), at<char>(ws, L.Qb)};
   int xspow = 1;  // the current X is the unnormalised input: scale by s once
   int xdt = io;   // dtype of the current X; normalised restarts store it in the iterate dtype
-  const int64_t nn = (int64_t)g.n * g.ldn;
 
-  Prod q = gram_prod(Xrow, xdt, g, R, it, sv, 2);
-  if (int st = run_prod(q, nb, K_SYRK, s)) return st;
+  if (int st = run_all(P, np, K_SYRK, s, [&](int i) {
+        return gram_prod(B[i].Xrow, xdt, P[i].g, B[i].R, it, B[i].sv, 2);
+      })) return st;
 
   bool q_fresh = true;
   int qcur = 0;
@@ -604,19 +684,18 @@ int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b
     const float a_k = c.coeff[k - 1][0], b_k = c.coeff[k - 1][1], c_k = c.coeff[k - 1][2];
     const bool restart = restart_at(c, k);
     const bool need_rect = restart || k == c.steps;
-    // Z = a I + b R + c R^2
-    char* zdst;
-    int zdt = it;
-    if (q_fresh) {
-      zdst = Qbuf[0];
-      zdt = need_rect ? xdt : it;
-    } else {
-      zdst = Z;
-    }
-    q = sym_prod(R, R, it, g, zdst, zdt);
-    q.c0 = a_k; q.c1 = b_k; q.c2 = c_k;
-    q.E = R; q.e_dt = it; q.lde = g.ldn; q.sE = nn; q.e_rows = g.n; q.e_cols = (int)g.ldn;
-    if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+    // Z = a I + b R + c R^2 (straight into Q when Q is the identity)
+    const bool zq = q_fresh;
+    const int zdt = q_fresh && need_rect ? xdt : it;
+    auto zdst = [&](int i) { return zq ? B[i].Qbuf[0] : B[i].Z; };
+    if (int st = run_all(P, np, K_SYMPROD, s, [&](int i) {
+          const Geo& g = P[i].g;
+          Prod q = sym_prod(B[i].R, B[i].R, it, g, zdst(i), zdt);
+          q.c0 = a_k; q.c1 = b_k; q.c2 = c_k;
+          q.E = B[i].R; q.e_dt = it; q.lde = g.ldn; q.sE = (int64_t)g.n * g.ldn; q.e_rows = g.n;
+          q.e_cols = (int)g.ldn;
+          return q;
+        })) return st;
     if (q_fresh) {
       qcur = 0;
       q_fresh = false;
@@ -627,58 +706,122 @@ int run_gram(const Geo& g, const NsConf& c, const Layout& L, void* ws, int64_t b
       // iterates add. Between updates the buffer holds Q^T, so both forms are NT products:
       // Q^T_new = Q^T Z, and Q_new = Z (Q^T)^T when Q goes on to multiply X.
       const int nxt = qcur ^ 1;
-      q = need_rect ? square_prod(zdst, Qbuf[qcur], it, g, Qbuf[nxt], xdt)
-                    : square_prod(Qbuf[qcur], zdst, it, g, Qbuf[nxt], it);
-      if (int st = run_prod(q, nb, K_SQUARE, s)) return st;
+      if (int st = run_all(P, np, K_SQUARE, s, [&](int i) {
+            return need_rect ? square_prod(zdst(i), B[i].Qbuf[qcur], it, P[i].g, B[i].Qbuf[nxt], xdt)
+                             : square_prod(B[i].Qbuf[qcur], zdst(i), it, P[i].g, B[i].Qbuf[nxt], it);
+          })) return st;
       qcur = nxt;
     }
     if (restart) {
       // X <- Q X (explicit), R <- X X^T, Q <- I
-      q = rect_prod(Qbuf[qcur], Xtb[xt], xdt, g);
-      q.svec = sv; q.spow = xspow;
-      set_internal_x_out(q, Xrow, Xtb[xt ^ 1], it, g);
-      if (int st = run_prod(q, nb, K_RECT, s)) return st;
+      if (int st = run_all(P, np, K_RECT, s, [&](int i) {
+            Prod q = rect_prod(B[i].Qbuf[qcur], B[i].Xtb[xt], xdt, P[i].g);
+            q.svec = B[i].sv; q.spow = xspow;
+            set_internal_x_out(q, B[i].Xrow, B[i].Xtb[xt ^ 1], it, P[i].g);
+            return q;
+          })) return st;
       xt ^= 1;
       xspow = 0;
       xdt = it;
-      q = gram_prod(Xrow, xdt, g, R, it, sv, 0);
-      if (int st = run_prod(q, nb, K_SYRK, s)) return st;
+      if (int st = run_all(P, np, K_SYRK, s, [&](int i) {
+            return gram_prod(B[i].Xrow, xdt, P[i].g, B[i].R, it, B[i].sv, 0);
+          })) return st;
       q_fresh = true;
     } else if (k < c.steps) {
       // W = R Z, R <- Z W
-      q = sym_prod(R, zdst, it, g, Wb, it);
-      if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
-      q = sym_prod(zdst, Wb, it, g, R, it);
-      if (int st = run_prod(q, nb, K_SYMPROD, s)) return st;
+      if (int st = run_all(P, np, K_SYMPROD, s, [&](int i) {
+            return sym_prod(B[i].R, zdst(i), it, P[i].g, B[i].Wb, it);
+          })) return st;
+      if (int st = run_all(P, np, K_SYMPROD, s, [&](int i) {
+            return sym_prod(zdst(i), B[i].Wb, it, P[i].g, B[i].R, it);
+          })) return st;
     }
     if (trace && k < c.steps) {
-      if (int st = trace_copy(R, it, g, trace + (int64_t)(k - 1) * g.n * g.n, s)) return st;
+      const Geo& g = P[0].g;
+      if (int st = trace_copy(B[0].R, it, g, trace + (int64_t)(k - 1) * g.n * g.n, s)) return st;
     }
   }
   // output = s^xspow Q X
-  q = rect_prod(Qbuf[qcur], Xtb[xt], xdt, g);
-  q.svec = sv; q.spow = xspow;
-  set_final(q, fo, g, b0);
-  return run_prod(q, nb, K_RECT, s);
+  return run_all(P, np, K_RECT, s, [&](int i) {
+    Prod q = rect_prod(B[i].Qbuf[qcur], B[i].Xtb[xt], xdt, P[i].g);
+    q.svec = B[i].sv; q.spow = xspow;
+    set_final(q, P[i].fo, P[i].g, P[i].b0);
+    return q;
+  });
 }
 
+int run_parts(int variant, Part* P, int np, const NsConf& c, int32_t* const* flags, hipStream_t s,
+              float* trace) {
+  for (int i = 0; i < np; ++i) {
+    if (int st = run_prep(P[i].src, P[i].g, c, P[i].L, P[i].ws, P[i].b0, P[i].nb, flags[i], s)) return st;
+    P[i].fo.flags = flags[i];
+  }
+  return variant == MNS_VARIANT_STANDARD ? run_standard(P, np, c, s) : run_gram(P, np, c, s, trace);
+}
+
+// One group, processed in the largest batch chunks that fit the workspace.
 int run_ns(int variant, const Source& src, const FinalOut& fo, const NsConf& c, void* ws,
            size_t ws_bytes, int32_t* flags, hipStream_t s, float* trace = nullptr) {
-  const Geo g = geometry(src.G);
+  Part P;
+  P.g = geometry(src.G);
   const int64_t batch = src.G->batch;
-  const int64_t chunk = pick_chunk(variant, g, c, batch, ws_bytes);
+  const int64_t chunk = pick_chunk(variant, P.g, c, batch, ws_bytes);
   if (chunk < 1) return MNS_ERR_WORKSPACE;
-  const Layout L = plan(variant, g, c, chunk);
+  P.L = plan(variant, P.g, c, chunk);
+  P.ws = reinterpret_cast<char*>(ws);
+  P.src = src;
   for (int64_t b0 = 0; b0 < batch; b0 += chunk) {
-    const int64_t nb = std::min(chunk, batch - b0);
-    if (int st = run_prep(src, g, c, L, ws, b0, nb, flags, s)) return st;
-    FinalOut f = fo;
-    f.flags = flags;
-    int st = variant == MNS_VARIANT_STANDARD ? run_standard(g, c, L, ws, b0, nb, f, s)
-                                             : run_gram(g, c, L, ws, b0, nb, f, s, trace);
-    if (st) return st;
+    P.b0 = b0;
+    P.nb = std::min(chunk, batch - b0);
+    P.fo = fo;
+    int32_t* fl[1] = {flags};
+    if (int st = run_parts(variant, &P, 1, c, fl, s, trace)) return st;
   }
   return MNS_OK;
+}
+
+// Workspace for processing ng groups side by side, each as one whole-batch chunk.
+size_t grouped_bytes(int variant, int ng, const mns_tensor* G, const NsConf& c) {
+  size_t tot = 0;
+  for (int i = 0; i < ng; ++i) tot = align256(tot + plan(variant, geometry(&G[i]), c, G[i].batch).total);
+  return tot;
+}
+
+// ng groups: side by side (every product one launch over all groups) when the workspace
+// holds them all at once, else one group after another (each chunked as needed).
+int run_groups(int variant, int ng, const Source* srcs, const FinalOut* fos, const NsConf& c,
+               void* ws, size_t ws_bytes, int32_t* flags, hipStream_t s) {
+  const mns_tensor* Gs[MNS_MAXG];
+  int64_t foff[MNS_MAXG];
+  int64_t off = 0;
+  for (int i = 0; i < ng; ++i) {
+    Gs[i] = srcs[i].G;
+    foff[i] = off;
+    off += srcs[i].G->batch;
+  }
+  size_t need = 0;
+  for (int i = 0; i < ng; ++i) need = align256(need + plan(variant, geometry(Gs[i]), c, Gs[i]->batch).total);
+  if (need > ws_bytes) {
+    for (int i = 0; i < ng; ++i)
+      if (int st = run_ns(variant, srcs[i], fos[i], c, ws, ws_bytes, flags ? flags + foff[i] : nullptr, s))
+        return st;
+    return MNS_OK;
+  }
+  Part P[MNS_MAXG];
+  int32_t* fl[MNS_MAXG];
+  size_t woff = 0;
+  for (int i = 0; i < ng; ++i) {
+    P[i].g = geometry(Gs[i]);
+    P[i].L = plan(variant, P[i].g, c, Gs[i]->batch);
+    P[i].ws = reinterpret_cast<char*>(ws) + woff;
+    woff = align256(woff + P[i].L.total);
+    P[i].b0 = 0;
+    P[i].nb = Gs[i]->batch;
+    P[i].src = srcs[i];
+    P[i].fo = fos[i];
+    fl[i] = flags ? flags + foff[i] : nullptr;
+  }
+  return run_parts(variant, P, ng, c, fl, s, nullptr);
 }
 
 int ns_entry(int variant, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
@@ -696,6 +839,52 @@ int ns_entry(int variant, const mns_tensor* G, const mns_tensor* O, const mns_ns
   FinalOut fo;
   fo.O = O;
   return run_ns(variant, src, fo, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Validation shared by the single and grouped Muon step.
+int check_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, const mns_tensor* U_out) {
+  if (int st = check_tensor(W)) return st;
+  if (int st = check_tensor(G)) return st;
+  if (int st = check_tensor(M)) return st;
+  if (!same_shape(W, G) || !same_shape(M, G)) return MNS_ERR_SHAPE;
+  if (M->dtype != F32) return MNS_ERR_DTYPE;
+  if (U_out) {
+    if (int st = check_tensor(U_out)) return st;
+    if (!same_shape(U_out, G)) return MNS_ERR_SHAPE;
+    if (overlap(U_out, W) || overlap(U_out, G) || overlap(U_out, M)) return MNS_ERR_ARG;
+  }
+  if (overlap(W, G) || overlap(W, M) || overlap(G, M)) return MNS_ERR_ARG;
+  return MNS_OK;
+}
+
+int check_step_params(const mns_step_params* sp) {
+  if (!sp) return MNS_ERR_ARG;
+  if (sp->variant != MNS_VARIANT_STANDARD && sp->variant != MNS_VARIANT_GRAM) return MNS_ERR_ARG;
+  const float vals[4] = {sp->lr, sp->momentum, sp->weight_decay, sp->scale_coeff};
+  for (float v : vals)
+    if (!std::isfinite(v)) return MNS_ERR_ARG;
+  return MNS_OK;
+}
+
+void step_io(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, const mns_tensor* U_out,
+             const mns_step_params* sp, Source* src, FinalOut* fo) {
+  src->G = G;
+  src->M = M;
+  src->mu = sp->momentum;
+  src->nesterov = sp->nesterov ? 1 : 0;
+  fo->W = W;
+  fo->U = U_out;
+  fo->u_scale = sp->scale_coeff * (float)std::sqrt((double)std::max(W->rows, W->cols));
+  fo->lr = sp->lr;
+  fo->wd_mul = (float)(1.0 - (double)sp->lr * (double)sp->weight_decay);
+}
+
+// Any two of the listed buffers overlap.
+bool any_overlap(const mns_tensor* const* t, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (t[i] && t[j] && overlap(t[i], t[j])) return true;
+  return false;
 }
 
 }  // namespace
@@ -729,37 +918,93 @@ int gram_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_param
 int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, const mns_tensor* U_out,
               const mns_step_params* sp, const mns_ns_params* p, void* ws, size_t ws_bytes,
               int32_t* flags, void* stream) {
-  if (int st = check_tensor(W)) return st;
-  if (int st = check_tensor(G)) return st;
-  if (int st = check_tensor(M)) return st;
-  if (!sp) return MNS_ERR_ARG;
-  if (!same_shape(W, G) || !same_shape(M, G)) return MNS_ERR_SHAPE;
-  if (M->dtype != F32) return MNS_ERR_DTYPE;
-  if (U_out) {
-    if (int st = check_tensor(U_out)) return st;
-    if (!same_shape(U_out, G)) return MNS_ERR_SHAPE;
-    if (overlap(U_out, W) || overlap(U_out, G) || overlap(U_out, M)) return MNS_ERR_ARG;
-  }
-  if (overlap(W, G) || overlap(W, M) || overlap(G, M)) return MNS_ERR_ARG;
-  if (sp->variant != MNS_VARIANT_STANDARD && sp->variant != MNS_VARIANT_GRAM) return MNS_ERR_ARG;
-  const float vals[4] = {sp->lr, sp->momentum, sp->weight_decay, sp->scale_coeff};
-  for (float v : vals)
-    if (!std::isfinite(v)) return MNS_ERR_ARG;
+  if (int st = check_step(W, G, M, U_out)) return st;
+  if (int st = check_step_params(sp)) return st;
   NsConf c;
   if (int st = check_params(p, G->dtype, &c)) return st;
   if (!ws) return MNS_ERR_WORKSPACE;
   Source src;
-  src.G = G;
-  src.M = M;
-  src.mu = sp->momentum;
-  src.nesterov = sp->nesterov ? 1 : 0;
   FinalOut fo;
-  fo.W = W;
-  fo.U = U_out;
-  fo.u_scale = sp->scale_coeff * (float)std::sqrt((double)std::max(W->rows, W->cols));
-  fo.lr = sp->lr;
-  fo.wd_mul = (float)(1.0 - (double)sp->lr * (double)sp->weight_decay);
+  step_io(W, G, M, U_out, sp, &src, &fo);
   return run_ns(sp->variant, src, fo, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mns_workspace_bytes_grouped(int variant, int ngroups, const mns_tensor* G, const mns_ns_params* p,
+                                size_t* bytes) {
+  if (!bytes || !G) return MNS_ERR_ARG;
+  if (variant != MNS_VARIANT_STANDARD && variant != MNS_VARIANT_GRAM) return MNS_ERR_ARG;
+  if (ngroups < 1 || ngroups > MNS_MAXG) return MNS_ERR_ARG;
+  for (int i = 0; i < ngroups; ++i) {
+    if (int st = check_tensor(&G[i], false)) return st;
+    if (G[i].dtype != G[0].dtype) return MNS_ERR_DTYPE;
+  }
+  NsConf c;
+  if (int st = check_params(p, G[0].dtype, &c)) return st;
+  *bytes = grouped_bytes(variant, ngroups, G, c);
+  return MNS_OK;
+}
+
+int muon_step_grouped(int ngroups, const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
+                      const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
+                      void* ws, size_t ws_bytes, int32_t* flags, void* stream) {
+  if (ngroups < 1 || ngroups > MNS_MAXG || !W || !G || !M) return MNS_ERR_ARG;
+  if (int st = check_step_params(sp)) return st;
+  const mns_tensor* all[4 * MNS_MAXG];
+  int na = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    if (int st = check_step(&W[i], &G[i], &M[i], U_out ? &U_out[i] : nullptr)) return st;
+    if (G[i].dtype != G[0].dtype) return MNS_ERR_DTYPE;
+    all[na++] = &W[i];
+    all[na++] = &G[i];
+    all[na++] = &M[i];
+    if (U_out) all[na++] = &U_out[i];
+  }
+  if (any_overlap(all, na)) return MNS_ERR_ARG;
+  NsConf c;
+  if (int st = check_params(p, G[0].dtype, &c)) return st;
+  if (!ws) return MNS_ERR_WORKSPACE;
+  Source srcs[MNS_MAXG];
+  FinalOut fos[MNS_MAXG];
+  for (int i = 0; i < ngroups; ++i) step_io(&W[i], &G[i], &M[i], U_out ? &U_out[i] : nullptr, sp, &srcs[i], &fos[i]);
+  return run_groups(sp->variant, ngroups, srcs, fos, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+static int ns_grouped(int variant, int ngroups, const mns_tensor* G, const mns_tensor* O,
+                      const mns_ns_params* p, void* ws, size_t ws_bytes, int32_t* flags, void* stream) {
+  if (ngroups < 1 || ngroups > MNS_MAXG || !G || !O) return MNS_ERR_ARG;
+  const mns_tensor* all[2 * MNS_MAXG];
+  int na = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    if (int st = check_tensor(&G[i])) return st;
+    if (int st = check_tensor(&O[i])) return st;
+    if (!same_shape(&G[i], &O[i])) return MNS_ERR_SHAPE;
+    if (O[i].dtype != G[i].dtype || G[i].dtype != G[0].dtype) return MNS_ERR_DTYPE;
+    all[na++] = &O[i];
+  }
+  if (any_overlap(all, na)) return MNS_ERR_ARG;
+  for (int i = 0; i < ngroups; ++i)
+    for (int j = 0; j < ngroups; ++j)
+      if (overlap(&G[i], &O[j])) return MNS_ERR_ARG;
+  NsConf c;
+  if (int st = check_params(p, G[0].dtype, &c)) return st;
+  if (!ws) return MNS_ERR_WORKSPACE;
+  Source srcs[MNS_MAXG];
+  FinalOut fos[MNS_MAXG];
+  for (int i = 0; i < ngroups; ++i) {
+    srcs[i].G = &G[i];
+    fos[i].O = &O[i];
+  }
+  return run_groups(variant, ngroups, srcs, fos, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+int muon_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+                    void* ws, size_t ws_bytes, int32_t* flags, void* stream) {
+  return ns_grouped(MNS_VARIANT_STANDARD, ngroups, G, O, p, ws, ws_bytes, flags, stream);
+}
+
+int gram_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+                    void* ws, size_t ws_bytes, int32_t* flags, void* stream) {
+  return ns_grouped(MNS_VARIANT_GRAM, ngroups, G, O, p, ws, ws_bytes, flags, stream);
 }
 
 int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,

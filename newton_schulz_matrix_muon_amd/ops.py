@@ -69,6 +69,13 @@ def _lib():
         lib.muon_step.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
                                   P(MnsStepParams), P(MnsNsParams), vp, sz, vp, vp]
         lib.gram_ns_trace.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
+        lib.mns_workspace_bytes_grouped.argtypes = [ctypes.c_int, ctypes.c_int, P(MnsTensor),
+                                                    P(MnsNsParams), P(sz)]
+        for fn in (lib.muon_ns_grouped, lib.gram_ns_grouped):
+            fn.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
+        lib.muon_step_grouped.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsTensor),
+                                          P(MnsTensor), P(MnsStepParams), P(MnsNsParams), vp, sz,
+                                          vp, vp]
         lib.mns_status_string.argtypes = [ctypes.c_int]
         lib.mns_status_string.restype = ctypes.c_char_p
         lib.mns_last_hip_error.argtypes = []
@@ -80,6 +87,8 @@ def _lib():
         lib.mns_kernel_kind_name.argtypes = [ctypes.c_int]
         lib.mns_kernel_kind_name.restype = ctypes.c_char_p
         for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched, lib.gram_ns_trace,
+                  lib.mns_workspace_bytes_grouped, lib.muon_ns_grouped, lib.gram_ns_grouped,
+                  lib.muon_step_grouped,
                   lib.muon_step, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
                   lib.mns_timing_reset, lib.mns_timing_query, lib.mns_timing_kinds):
             f.restype = ctypes.c_int
@@ -212,6 +221,77 @@ def muon_step(W, G, M, *, lr: float, momentum: float, weight_decay: float,
                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), fptr, _stream_ptr(G)),
            "muon_step")
     return W
+
+
+# ------------------------------------------------------------------ grouped calls
+MAX_GROUPS = 4
+
+
+def _tensor_array(ts):
+    arr = (MnsTensor * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t if isinstance(t, MnsTensor) else describe(t)
+    return arr
+
+
+def workspace_bytes_grouped(variant: int, Gs, params: MnsNsParams) -> int:
+    """Workspace that lets a grouped call process every group side by side."""
+    n = ctypes.c_size_t()
+    _check(_lib().mns_workspace_bytes_grouped(variant, len(Gs), _tensor_array(Gs), ctypes.byref(params),
+                                              ctypes.byref(n)), "mns_workspace_bytes_grouped")
+    return n.value
+
+
+def _ns_grouped(variant, Gs, outs, params, workspace, flags):
+    torch = _torch()
+    outs = [torch.empty_like(G) for G in Gs] if outs is None else list(outs)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_grouped(variant, Gs, params), dtype=torch.uint8,
+                                device=Gs[0].device)
+    fn = _lib().muon_ns_grouped if variant == STANDARD else _lib().gram_ns_grouped
+    fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
+    _check(fn(len(Gs), _tensor_array(Gs), _tensor_array(outs), ctypes.byref(params),
+              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), fptr, _stream_ptr(Gs[0])),
+           "muon_ns_grouped" if variant == STANDARD else "gram_ns_grouped")
+    return outs
+
+
+def muon_ns_grouped(Gs, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+                    iter_dtype: Optional[int] = None, outs=None, workspace=None, flags=None):
+    """Standard Newton-Schulz of several batches of different shapes (C ABI ``muon_ns_grouped``)."""
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(Gs[0]), 0)
+    return _ns_grouped(STANDARD, Gs, outs, p, workspace, flags)
+
+
+def gram_ns_grouped(Gs, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+                    iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK,
+                    outs=None, workspace=None, flags=None):
+    """Gram Newton-Schulz of several batches of different shapes (C ABI ``gram_ns_grouped``)."""
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(Gs[0]), restart_mask)
+    return _ns_grouped(GRAM, Gs, outs, p, workspace, flags)
+
+
+def muon_step_grouped(Ws, Gs, Ms, *, lr: float, momentum: float, weight_decay: float,
+                      scale_coeff: float = 0.2, nesterov: bool = False, variant: int = GRAM,
+                      steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+                      iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK,
+                      U_outs=None, workspace=None, flags=None):
+    """One fused Muon step over several batches of different shapes (C ABI
+    ``muon_step_grouped``); every W and M is updated in place."""
+    torch = _torch()
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(Gs[0]),
+                  restart_mask if variant == GRAM else 0)
+    sp = MnsStepParams(lr, momentum, weight_decay, scale_coeff, 1 if nesterov else 0, variant)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_grouped(variant, Gs, p), dtype=torch.uint8,
+                                device=Gs[0].device)
+    fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
+    u = _tensor_array(U_outs) if U_outs is not None else None
+    _check(_lib().muon_step_grouped(len(Gs), _tensor_array(Ws), _tensor_array(Gs), _tensor_array(Ms),
+                                    u, ctypes.byref(sp), ctypes.byref(p),
+                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), fptr,
+                                    _stream_ptr(Gs[0])), "muon_step_grouped")
+    return Ws
 
 
 def gram_trace(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,

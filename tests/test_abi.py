@@ -137,3 +137,42 @@ def test_timing_api_without_launches(L):
     assert L.mns_kernel_kind_name(99) is None
     ops.timing_reset()
     assert all(v == (0.0, 0) for v in ops.timing_query().values())
+
+
+def test_grouped_argument_errors(L):
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    sp = ops.MnsStepParams(0.02, 0.95, 0.01, 0.2, 1, ops.GRAM)
+    Ws = ops._tensor_array([_t(ops, ptr=0x100000), _t(ops, ptr=0x400000, rows=16, cols=8)])
+    Gs = ops._tensor_array([_t(ops, ptr=0x200000), _t(ops, ptr=0x500000, rows=16, cols=8)])
+    Ms = ops._tensor_array([_t(ops, ptr=0x300000, dtype=0), _t(ops, ptr=0x600000, dtype=0, rows=16, cols=8)])
+    ws = ctypes.c_void_p(0x7f0000000000)
+    f = lambda n=2, w=Ws, g=Gs, m=Ms, wsp=ws: L.muon_step_grouped(
+        n, w, g, m, None, ctypes.byref(sp), ctypes.byref(p), wsp, 1 << 40, None, None)
+    assert f(n=0) == -1 and f(n=5) == -1                               # 1 .. 4 groups
+    assert f(wsp=None) == -4
+    W_ov = ops._tensor_array([_t(ops, ptr=0x100000), _t(ops, ptr=0x100000 + 64, rows=16, cols=8)])
+    assert f(w=W_ov) == -1                                             # outputs overlap across groups
+    G_dt = ops._tensor_array([_t(ops, ptr=0x200000), _t(ops, ptr=0x500000, rows=16, cols=8, dtype=2)])
+    W_dt = ops._tensor_array([_t(ops, ptr=0x100000), _t(ops, ptr=0x400000, rows=16, cols=8, dtype=2)])
+    assert f(w=W_dt, g=G_dt) == -2                                     # one input dtype for all groups
+    Os = ops._tensor_array([_t(ops, ptr=0x900000), _t(ops, ptr=0x200000 + 32, rows=16, cols=8)])
+    assert L.gram_ns_grouped(2, Gs, Os, ctypes.byref(p), ws, 1 << 40, None, None) == -1   # output over an input
+    assert L.mns_last_hip_error() == 0
+
+
+def test_grouped_workspace_is_the_sum_of_the_groups(L):
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    groups = [_t(ops, batch=432, rows=2048, cols=7168), _t(ops, batch=216, rows=7168, cols=2048),
+              _t(ops, batch=3, rows=7168, cols=18432)]
+    for variant in (ops.STANDARD, ops.GRAM):
+        singles = []
+        for g in groups:
+            b = ctypes.c_size_t()
+            assert L.mns_workspace_bytes(variant, ctypes.byref(g), ctypes.byref(p), 0, ctypes.byref(b)) == 0
+            singles.append(b.value)
+        tot = ctypes.c_size_t()
+        assert L.mns_workspace_bytes_grouped(variant, 3, ops._tensor_array(groups), ctypes.byref(p),
+                                             ctypes.byref(tot)) == 0
+        assert sum(singles) <= tot.value <= sum(singles) + 3 * 256
