@@ -18,3 +18,4 @@ from .ns import (  # noqa: F401
     scalar_ns_map,
     muon_step,
 )
+from .adamw import adamw_step  # noqa: F401

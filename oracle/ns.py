@@ -23,7 +23,7 @@ Sources (web pages):
   instability of the naive Gram form, and the stabilized variant that restarts
   after step 2 and re-forms the Gram matrix.
 
-Readings of points the pages leave open (also listed in the design doc):
+Readings of points the pages leave open:
 * coefficients: one triple (a_k, b_k, c_k) per step; the step maps
   X -> a X + b (X X^T) X + c (X X^T)^2 X, i.e. each singular value s -> a s + b s^3 + c s^5.
   Default: the quintic (3.4445, -4.7750, 2.0315) for every step; the pages' own
