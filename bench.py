@@ -47,6 +47,63 @@ def kind_work(kind: str, groups):
     return sum(B * f(n, m) for B, n, m in groups), unit, bound
 
 
+ADAMW_KW = dict(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def adamw_params(torch, dev):
+    """The Kimi-K2 parameters that stay on AdamW (guide, hybrid strategy): the 163840 x 7168
+    token embedding, 60 router projections 384 x 7168, and 122 RMSNorm scales of 7168 (bf16
+    parameters and gradients, fp32 moments)."""
+    sizes = [163840 * 7168] + [384 * 7168] * 60 + [7168] * 122
+    gen = torch.Generator(device=dev).manual_seed(4242)
+    out = []
+    for n in sizes:
+        p = (0.02 * torch.randn(n, generator=gen, device=dev)).to(torch.bfloat16)
+        g = (1e-3 * torch.randn(n, generator=gen, device=dev)).to(torch.bfloat16)
+        out.append((p, g, torch.zeros(n, device=dev), torch.zeros(n, device=dev)))
+    return out
+
+
+def bench_adamw(args):
+    """AdamW on the Kimi-K2 1-D / embedding parameters alone: parameter updates per second and
+    the kernel's HBM roofline (22 bytes per bf16 parameter: read p, g, m, v; write p, m, v)."""
+    import torch
+    from newton_schulz_matrix_muon_amd import ops
+    dev = torch.device("cuda:0")
+    vec = adamw_params(torch, dev)
+    ps, gs, ms, vs = (list(x) for x in zip(*vec))
+    numel = sum(p.numel() for p in ps)
+    for _ in range(args.warmup):
+        ops.adamw_step(ps, gs, ms, vs, **ADAMW_KW)
+    torch.cuda.synchronize()
+    ops.timing_reset()
+    ops.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ops.adamw_step(ps, gs, ms, vs, **ADAMW_KW)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    ops.timing_enable(False)
+    ms_tot, launches = ops.timing_query()["adamw"]
+    per_launch = launches // args.steps
+    # the embedding is the first launch's dominant tensor; per launch bytes = its tensors' bytes
+    step_bytes = 22 * numel
+    avg_s = ms_tot / launches / 1e3
+    achieved = step_bytes / per_launch / avg_s / 1e9
+    out = {"metric": "AdamW parameter updates/sec (hybrid optimizer, 1-D and embedding side)",
+           "value": numel / sec, "unit": "parameters/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "kimi_k2_adamw_embedding_163840x7168+60x384x7168+122x7168_bf16",
+                      "parameters": numel, **ADAMW_KW},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "adamw",
+                        "avg_launch_ms": avg_s * 1e3, "launches": launches,
+                        "note": "bytes per launch averaged over the step's launches"},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources (name + bytes, sorted): ties recorded counters to a build."""
     import hashlib
@@ -115,10 +172,12 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--variant", choices=["gram", "standard"], default="gram")
-    ap.add_argument("--workload", choices=["experts", "k2_full"], default="experts",
+    ap.add_argument("--workload", choices=["experts", "k2_full", "k2_hybrid", "adamw"], default="experts",
                     help="experts: one batch of --batch x --rows x --cols expert matrices (default "
-                         "648 x 2048 x 7168); k2_full: the whole Kimi-K2 step in one grouped call "
-                         "(432 x 2048 x 7168 up/gate, 216 x 7168 x 2048 down, 3 x 7168 x 18432 dense)")
+                         "648 x 2048 x 7168); k2_full: the whole Kimi-K2 Muon step in one grouped call "
+                         "(432 x 2048 x 7168 up/gate, 216 x 7168 x 2048 down, 3 x 7168 x 18432 dense); "
+                         "k2_hybrid: k2_full plus AdamW on the 1-D / embedding parameters; adamw: the "
+                         "AdamW side alone")
     ap.add_argument("--batch", type=int, default=648)
     ap.add_argument("--rows", type=int, default=2048)
     ap.add_argument("--cols", type=int, default=7168)
@@ -143,12 +202,17 @@ def main():
     if args.copy_probe_mib > 0:
         log(f"copy probe: {args.copy_probe_mib} MiB")
         copy_probe(args.copy_probe_mib)
+    if args.workload == "adamw":
+        return bench_adamw(args)
     if args.workload == "experts":
         shapes = [(args.batch, args.rows, args.cols)]
         workload = f"kimi_k2_experts_{args.batch}x{args.rows}x{args.cols}_bf16_gaussian_plus_rank32_spike"
     else:
         shapes = [(432, 2048, 7168), (216, 7168, 2048), (3, 7168, 18432)]
         workload = "kimi_k2_full_step_432x2048x7168+216x7168x2048+3x7168x18432_bf16_gaussian_plus_rank32_spike"
+        if args.workload == "k2_hybrid":
+            workload = "kimi_k2_hybrid_step_muon_" + workload[len("kimi_k2_full_step_"):] + "+adamw_1d_embedding"
+    vectors = adamw_params(torch, dev) if args.workload == "k2_hybrid" else None
     groups = [(B, min(r, c), max(r, c)) for B, r, c in shapes]
     total = sum(B for B, _, _ in shapes)
     Gs, Ws, Ms = [], [], []
@@ -178,8 +242,11 @@ def main():
     def step(variant_code):
         if len(shapes) == 1:
             ops.muon_step(Ws[0], Gs[0], Ms[0], variant=variant_code, workspace=ws, **steps_kw)
-        else:
+        elif vectors is None:
             ops.muon_step_grouped(Ws, Gs, Ms, variant=variant_code, workspace=ws, **steps_kw)
+        else:
+            ops.hybrid_step(list(zip(Ws, Gs, Ms)), vectors,
+                            muon=dict(variant=variant_code, workspace=ws, **steps_kw), adamw=ADAMW_KW)
 
     def timed(variant_code, steps, warmup, with_kernel_timing):
         for _ in range(warmup):

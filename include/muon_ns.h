@@ -176,6 +176,33 @@ int muon_step_grouped(int ngroups, const mns_tensor* W, const mns_tensor* G, con
                       void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
 /*
+ * AdamW for the parameters that stay off Muon (guide, "The Hybrid Optimization Strategy":
+ * RMSNorm scales, biases, router projections, token embeddings; update from "The
+ * Coordinate-Wise Limitation of AdamW"):
+ *   m <- beta1 m + (1 - beta1) g;  v <- beta2 v + (1 - beta2) g^2;
+ *   p <- (1 - lr weight_decay) p - lr m^ / (sqrt(v^) + eps),
+ * with m^ = m, v^ = v, or with bias_correction set m^ = m / (1 - beta1^step),
+ * v^ = v / (1 - beta2^step). eps is outside the square root, as in the guide's equation.
+ */
+typedef struct mns_adamw_params {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t step;             /* >= 1 (used by the bias correction only) */
+  int32_t bias_correction;  /* 0 or 1 */
+} mns_adamw_params;
+
+/*
+ * One AdamW step over ntensors flat, contiguous tensors (host arrays of device pointers):
+ * params[i] and grads[i] of `dtype` (F32, BF16 or F16; the same for all), exp_avg[i] and
+ * exp_avg_sq[i] fp32, all numels[i] elements long (0 allowed). params and both moments are
+ * updated in place; no two buffers may overlap. Tensors are processed 48 per launch.
+ * Errors: MNS_ERR_ARG (null pointer, numel < 0, non-finite or out-of-range hyper-parameter,
+ * beta outside [0, 1), overlap), MNS_ERR_DTYPE, MNS_ERR_HIP.
+ */
+int adamw_step(int ntensors, void* const* params, const void* const* grads, float* const* exp_avg,
+               float* const* exp_avg_sq, const int64_t* numels, int32_t dtype,
+               const mns_adamw_params* ap, void* stream);
+
+/*
  * Debug trace of the Gram iteration for the first matrix of G (diagnostics of the fp16
  * instability the Gram Newton-Schulz article describes: negative eigenvalues of the Gram
  * matrix). Runs gram_ns_batched on matrix 0 only and, after each step k = 1 .. K-1, copies the

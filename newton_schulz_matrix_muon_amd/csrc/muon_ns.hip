@@ -18,6 +18,7 @@
 #include "common.hpp"
 #include "elementwise.hpp"
 #include "gemm.hpp"
+#include "adamw.hpp"
 
 using namespace mns;
 
@@ -26,9 +27,9 @@ namespace {
 thread_local int g_last_hip = 0;
 
 // ------------------------------------------------------------------ launch timing
-enum Kind { K_PREP = 0, K_FINALIZE, K_SYRK, K_SYMPROD, K_RECT, K_CAST, K_SQUARE, NKINDS };
-const char* const kKindNames[NKINDS] = {"prep_norm", "finalize_norm", "gemm_syrk",
-                                        "gemm_symprod", "gemm_rect", "cast", "gemm_square"};
+enum Kind { K_PREP = 0, K_FINALIZE, K_SYRK, K_SYMPROD, K_RECT, K_CAST, K_SQUARE, K_ADAMW, NKINDS };
+const char* const kKindNames[NKINDS] = {"prep_norm", "finalize_norm", "gemm_syrk", "gemm_symprod",
+                                        "gemm_rect", "cast", "gemm_square", "adamw"};
 
 struct Timing {
   std::mutex mu;
@@ -887,6 +888,49 @@ bool any_overlap(const mns_tensor* const* t, int n) {
   return false;
 }
 
+int run_adamw(int nt, void* const* params, const void* const* grads, float* const* m, float* const* v,
+              const int64_t* numels, int dt, const mns_adamw_params* ap, hipStream_t s) {
+  AdamTable t;
+  t.lr = ap->lr;
+  t.beta1 = ap->beta1;
+  t.beta2 = ap->beta2;
+  t.eps = ap->eps;
+  t.wd_mul = (float)(1.0 - (double)ap->lr * (double)ap->weight_decay);
+  t.bc1 = ap->bias_correction ? (float)(1.0 / (1.0 - std::pow((double)ap->beta1, ap->step))) : 1.f;
+  t.bc2 = ap->bias_correction ? (float)(1.0 / (1.0 - std::pow((double)ap->beta2, ap->step))) : 1.f;
+  int i = 0;
+  while (i < nt) {
+    int k = 0;
+    int64_t blocks = 0;
+    for (; i < nt && k < ADAM_MAXT; ++i) {
+      if (numels[i] == 0) continue;
+      const int64_t b = (numels[i] + ADAM_CHUNK - 1) / ADAM_CHUNK;
+      if (blocks + b > INT32_MAX) break;
+      t.p[k] = params[i];
+      t.g[k] = grads[i];
+      t.m[k] = m[i];
+      t.v[k] = v[i];
+      t.numel[k] = numels[i];
+      t.blk_start[k] = (int)blocks;
+      blocks += b;
+      ++k;
+    }
+    if (k == 0) {
+      if (i < nt && numels[i] > 0) return MNS_ERR_SHAPE;   // one tensor beyond INT32_MAX blocks
+      continue;
+    }
+    t.blk_start[k] = (int)blocks;
+    t.nt = k;
+    if (int st = launch(K_ADAMW, s, [&] {
+          if (dt == F32) hipLaunchKernelGGL(adamw_kernel<float>, dim3((unsigned)blocks), dim3(ADAM_BLOCK), 0, s, t);
+          else if (dt == BF16) hipLaunchKernelGGL(adamw_kernel<__bf16>, dim3((unsigned)blocks), dim3(ADAM_BLOCK), 0, s, t);
+          else hipLaunchKernelGGL(adamw_kernel<_Float16>, dim3((unsigned)blocks), dim3(ADAM_BLOCK), 0, s, t);
+        }))
+      return st;
+  }
+  return MNS_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -1028,6 +1072,37 @@ int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params*
   fo.O = &o1;
   return run_ns(MNS_VARIANT_GRAM, src, fo, c, ws, ws_bytes, nullptr,
                 reinterpret_cast<hipStream_t>(stream), trace);
+}
+
+int adamw_step(int ntensors, void* const* params, const void* const* grads, float* const* exp_avg,
+               float* const* exp_avg_sq, const int64_t* numels, int32_t dtype,
+               const mns_adamw_params* ap, void* stream) {
+  if (ntensors < 1 || !params || !grads || !exp_avg || !exp_avg_sq || !numels || !ap) return MNS_ERR_ARG;
+  if (!valid_dtype(dtype)) return MNS_ERR_DTYPE;
+  const float hp[5] = {ap->lr, ap->beta1, ap->beta2, ap->eps, ap->weight_decay};
+  for (float x : hp)
+    if (!std::isfinite(x)) return MNS_ERR_ARG;
+  if (ap->beta1 < 0.f || ap->beta1 >= 1.f || ap->beta2 < 0.f || ap->beta2 >= 1.f || ap->eps < 0.f) return MNS_ERR_ARG;
+  if (ap->bias_correction != 0 && ap->bias_correction != 1) return MNS_ERR_ARG;
+  if (ap->bias_correction && ap->step < 1) return MNS_ERR_ARG;
+  // every buffer non-null (unless empty) and no two buffers overlapping
+  std::vector<std::pair<uintptr_t, uintptr_t>> iv;
+  const size_t es = (size_t)dtype_size(dtype);
+  for (int i = 0; i < ntensors; ++i) {
+    if (numels[i] < 0) return MNS_ERR_ARG;
+    if (numels[i] == 0) continue;
+    if (!params[i] || !grads[i] || !exp_avg[i] || !exp_avg_sq[i]) return MNS_ERR_ARG;
+    const uintptr_t n = (uintptr_t)numels[i];
+    iv.push_back({reinterpret_cast<uintptr_t>(params[i]), reinterpret_cast<uintptr_t>(params[i]) + n * es});
+    iv.push_back({reinterpret_cast<uintptr_t>(grads[i]), reinterpret_cast<uintptr_t>(grads[i]) + n * es});
+    iv.push_back({reinterpret_cast<uintptr_t>(exp_avg[i]), reinterpret_cast<uintptr_t>(exp_avg[i]) + n * 4});
+    iv.push_back({reinterpret_cast<uintptr_t>(exp_avg_sq[i]), reinterpret_cast<uintptr_t>(exp_avg_sq[i]) + n * 4});
+  }
+  std::sort(iv.begin(), iv.end());
+  for (size_t k = 1; k < iv.size(); ++k)
+    if (iv[k].first < iv[k - 1].second) return MNS_ERR_ARG;
+  return run_adamw(ntensors, params, grads, exp_avg, exp_avg_sq, numels, dtype, ap,
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 const char* mns_status_string(int code) {

@@ -76,6 +76,10 @@ def _lib():
         lib.muon_step_grouped.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsTensor),
                                           P(MnsTensor), P(MnsStepParams), P(MnsNsParams), vp, sz,
                                           vp, vp]
+        pp = P(vp)
+        lib.adamw_step.argtypes = [ctypes.c_int, pp, pp, pp, pp, P(ctypes.c_int64), ctypes.c_int32,
+                                   P(MnsAdamwParams), vp]
+        lib.adamw_step.restype = ctypes.c_int
         lib.mns_status_string.argtypes = [ctypes.c_int]
         lib.mns_status_string.restype = ctypes.c_char_p
         lib.mns_last_hip_error.argtypes = []
@@ -292,6 +296,49 @@ def muon_step_grouped(Ws, Gs, Ms, *, lr: float, momentum: float, weight_decay: f
                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), fptr,
                                     _stream_ptr(Gs[0])), "muon_step_grouped")
     return Ws
+
+
+# ------------------------------------------------------------------ AdamW (hybrid optimizer)
+class MnsAdamwParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
+                ("bias_correction", ctypes.c_int32)]
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, beta1: float = 0.9,
+               beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.1, step: int = 1,
+               bias_correction: bool = False):
+    """One AdamW step over lists of contiguous tensors (C ABI ``adamw_step``); params and both
+    fp32 moments are updated in place."""
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n) or n == 0:
+        raise ValueError("params, grads and moments must be non-empty lists of equal length")
+    for group in (params, grads, exp_avgs, exp_avg_sqs):
+        for t in group:
+            if not t.is_contiguous():
+                raise ValueError("AdamW tensors must be contiguous")
+    for p_, g_, m_, v_ in zip(params, grads, exp_avgs, exp_avg_sqs):
+        if not (p_.numel() == g_.numel() == m_.numel() == v_.numel()):
+            raise ValueError("each parameter, gradient and moment pair must have equal sizes")
+    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+    numels = (ctypes.c_int64 * n)(*[t.numel() for t in params])
+    ap = MnsAdamwParams(lr, beta1, beta2, eps, weight_decay, step, 1 if bias_correction else 0)
+    _check(_lib().adamw_step(n, arr(params), arr(grads), arr(exp_avgs), arr(exp_avg_sqs), numels,
+                             dtype_code(params[0]), ctypes.byref(ap), _stream_ptr(params[0])),
+           "adamw_step")
+    return params
+
+
+def hybrid_step(matrix_groups, vector_params, *, muon: dict, adamw: dict):
+    """The hybrid optimizer step: Muon for the 2-D matrices (``matrix_groups``: list of
+    (W, G, M) batches, one grouped call) and AdamW for everything else (``vector_params``:
+    list of (param, grad, exp_avg, exp_avg_sq)), enqueued on the current stream."""
+    if matrix_groups:
+        Ws, Gs, Ms = (list(x) for x in zip(*matrix_groups))
+        muon_step_grouped(Ws, Gs, Ms, **muon)
+    if vector_params:
+        ps, gs, ms, vs = (list(x) for x in zip(*vector_params))
+        adamw_step(ps, gs, ms, vs, **adamw)
 
 
 def gram_trace(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,

@@ -176,3 +176,21 @@ def test_grouped_workspace_is_the_sum_of_the_groups(L):
         assert L.mns_workspace_bytes_grouped(variant, 3, ops._tensor_array(groups), ctypes.byref(p),
                                              ctypes.byref(tot)) == 0
         assert sum(singles) <= tot.value <= sum(singles) + 3 * 256
+
+
+def test_adamw_argument_errors(L):
+    from newton_schulz_matrix_muon_amd import ops
+    P = lambda *xs: (ctypes.c_void_p * len(xs))(*xs)
+    n = (ctypes.c_int64 * 2)(100, 50)
+    ok = ops.MnsAdamwParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1, 0)
+    args = [P(0x1000, 0x9000), P(0x2000, 0xa000), P(0x3000, 0xb000), P(0x4000, 0xc000)]
+    f = lambda a=args, nn=n, dt=1, ap=ok, nt=2: L.adamw_step(nt, *a, nn, dt, ctypes.byref(ap), None)
+    assert f(nt=0) == -1
+    assert f(dt=7) == -2
+    assert f(ap=ops.MnsAdamwParams(1e-3, 1.0, 0.95, 1e-8, 0.1, 1, 0)) == -1       # beta1 = 1
+    assert f(ap=ops.MnsAdamwParams(float("nan"), 0.9, 0.95, 1e-8, 0.1, 1, 0)) == -1
+    assert f(ap=ops.MnsAdamwParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 0, 1)) == -1       # step 0 with bias correction
+    assert f(a=[P(0x1000, 0x9000), P(0x1000 + 8, 0xa000), P(0x3000, 0xb000), P(0x4000, 0xc000)]) == -1  # p/g overlap
+    assert f(a=[P(0x1000, 0), P(0x2000, 0xa000), P(0x3000, 0xb000), P(0x4000, 0xc000)]) == -1            # null
+    assert f(nn=(ctypes.c_int64 * 2)(100, -1)) == -1
+    assert L.mns_last_hip_error() == 0
