@@ -107,9 +107,6 @@ struct TileCfg {
 // Large problems: 256 x 256, 16 waves of 64 x 64, 128-byte k-stages DMA'd global -> LDS into a
 // 2-deep ring, 4 waves per SIMD (one workgroup per CU; latency is hidden by the four waves
 // each SIMD interleaves).
-#ifndef MNS_FRAG_DB
-#define MNS_FRAG_DB 0
-#endif
 #ifndef MNS_CFG128
 #define MNS_CFG128 128, 128, 2, 2, 128, 1, 2
 #endif
@@ -300,92 +297,6 @@ __device__ inline void mma(const typename Frag<T>::type (&a)[TM], const typename
 constexpr uint32_t OOB = 0x80000000u;
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// scalar conversions and a 4-element (8- or 16-byte) store for the register-direct epilogue
-__device__ inline float to_f32(float x) { return x; }
-__device__ inline float to_f32(__bf16 x) { return bf16_bits_to_f32(__builtin_bit_cast(uint16_t, x)); }
-__device__ inline float to_f32(_Float16 x) { return (float)x; }
-template <typename OT> __device__ inline OT from_f32(float x);
-template <> __device__ inline float from_f32<float>(float x) { return x; }
-template <> __device__ inline __bf16 from_f32<__bf16>(float x) { return __builtin_bit_cast(__bf16, f32_to_bf16_bits(x)); }
-template <> __device__ inline _Float16 from_f32<_Float16>(float x) { return __builtin_bit_cast(_Float16, f32_to_f16_bits(x)); }
-template <typename OT>
-__device__ inline void store4(OT* p, const float (&v)[4]) {
-  if constexpr (sizeof(OT) == 4) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-  } else {
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 w;
-    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[0])) | ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[1])) << 16);
-    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[2])) | ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<OT>(v[3])) << 16);
-    *reinterpret_cast<u32x2*>(p) = w;
-  }
-}
-
-// Register-direct epilogue for internal outputs (same conditions as the staged fast path):
-// each lane stores from the MFMA accumulator layout — lanes l and l + 32 hold 4 consecutive
-// rows of one column — so row-major stores are one element per lane (a 64-byte run per row
-// across 32 lanes) and transposed / mirrored stores are 4 consecutive elements per lane.
-// No LDS and no barriers.
-template <typename OT, typename ET, bool TRI, class CFG>
-__device__ inline void epilogue_direct(const GemmArgs& p, f32x16 (&acc)[CFG::TM][CFG::TN],
-                                       int mat, int ti, int tj, int row0, int col0) {
-  constexpr int TM = CFG::TM, TN = CFG::TN, WTM = CFG::WTM, WTN = CFG::WTN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
-  float sc = 1.f;
-  if (p.spow) {
-    const float sb = p.svec[mat];
-    sc = p.spow == 1 ? sb : sb * sb;
-  }
-  const ET* Eb = p.E ? reinterpret_cast<const ET*>(p.E) + (int64_t)mat * p.sE : nullptr;
-  OT* Cb = p.C ? reinterpret_cast<OT*>(p.C) + (int64_t)mat * p.sC : nullptr;
-  OT* Ctb = p.Ct ? reinterpret_cast<OT*>(p.Ct) + (int64_t)mat * p.sCt : nullptr;
-  const bool diag = TRI && ti == tj;
-  const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
-  const int cl = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int c = col0 + wn * WTN + j * 32 + cl;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int rb = row0 + wm * WTM + i * 32 + 8 * q4 + 4 * hi;   // rows rb .. rb + 3
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rb + e;
-          float x = c2 * acc[i][j][4 * q4 + e];
-          if (Eb && r < p.e_rows && c < p.e_cols) x += c1 * to_f32(Eb[(int64_t)r * p.lde + c]);
-          x *= sc;
-          if (r == c && r < p.M) x += c0;
-          v[e] = x;
-        }
-        if (Cb && c < p.c_cols) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rb + e;
-            if (r < p.c_rows && (!diag || r <= c)) Cb[(int64_t)r * p.ldc + c] = from_f32<OT>(v[e]);
-          }
-        }
-        // transposed destination (c, rb .. rb + 3): the mirror of a symmetric result, or C^T
-        OT* Tp = TRI ? Cb : Ctb;
-        const int trows = TRI ? p.c_rows : p.ct_rows, tcols = TRI ? p.c_cols : p.ct_cols;
-        const int64_t tld = TRI ? p.ldc : p.ldct;
-        if (Tp && c < trows && rb < tcols) {
-          const bool whole = rb + 4 <= tcols && (!diag || rb + 3 < c);
-          if (whole) {
-            store4<OT>(Tp + (int64_t)c * tld + rb, v);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (rb + e < tcols && (!diag || rb + e < c)) Tp[(int64_t)c * tld + rb + e] = from_f32<OT>(v[e]);
-          }
-        }
-      }
-    }
 }
 
 // Fast epilogue for internal outputs: C (row-major; mirrored for symmetric results) and
@@ -674,7 +585,7 @@ gemm_nt_kernel(const GemmBatch gb) {
 
 
   typedef typename Frag<T>::type F;
-  F fa[MNS_FRAG_DB ? 2 : 1][TM], fb[MNS_FRAG_DB ? 2 : 1][TN];
+  F fa[TM], fb[TN];
   // Prologue: stage 0 in LDS, stages 1 .. PF-1 in flight in register sets 1 .. PF-1.
 #pragma unroll
   for (int s_ = 0; s_ < PF; ++s_)
@@ -693,21 +604,11 @@ gemm_nt_kernel(const GemmBatch gb) {
     if (kt + PF < nk) load_stage((kt + PF) * BK, set);
     const char* As = lds + cur * CFG::STAGE + (wm * WTM) * ROWB;
     const char* Bs = lds + cur * CFG::STAGE + (BM + wn * WTN) * ROWB;
-    if constexpr (MNS_FRAG_DB) {
-      // fragments of group g + 1 are read while group g's MFMAs run
-      load_frags<T, TM, TN, ROWB>(As, Bs, lane, 0, fa[0], fb[0]);
+    // one fragment set: the other waves of the SIMD cover the LDS latency
 #pragma unroll
-      for (int g = 0; g < CFG::NG; ++g) {
-        if (g + 1 < CFG::NG) load_frags<T, TM, TN, ROWB>(As, Bs, lane, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
-        mma<T, TM, TN>(fa[g & 1], fb[g & 1], acc);
-      }
-    } else {
-      // one fragment set: the other waves of the SIMD cover the LDS latency
-#pragma unroll
-      for (int g = 0; g < CFG::NG; ++g) {
-        load_frags<T, TM, TN, ROWB>(As, Bs, lane, g, fa[0], fb[0]);
-        mma<T, TM, TN>(fa[0], fb[0], acc);
-      }
+    for (int g = 0; g < CFG::NG; ++g) {
+      load_frags<T, TM, TN, ROWB>(As, Bs, lane, g, fa, fb);
+      mma<T, TM, TN>(fa, fb, acc);
     }
     if (kt + 1 < nk) store_stage(cur ^ 1, nset);
     __syncthreads();
@@ -738,17 +639,7 @@ gemm_nt_kernel(const GemmBatch gb) {
   }  // register-staged main loop
 
   // ---------------------------------------------------------------- epilogue
-#ifndef MNS_EPI_DIRECT
-#define MNS_EPI_DIRECT 0
-#endif
-  if constexpr (EPI != 0 && MNS_EPI_DIRECT) {
-    if constexpr (EPI == 1) epilogue_direct<_Float16, _Float16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 2) epilogue_direct<__bf16, __bf16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 3) epilogue_direct<_Float16, __bf16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 4) epilogue_direct<__bf16, _Float16, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
-    else epilogue_direct<float, float, TRI, CFG>(p, acc, mat, ti, tj, row0, col0);
-    continue;
-  } else if constexpr (EPI != 0) {
+  if constexpr (EPI != 0) {
     if constexpr (EPI == 1) epilogue_fast<_Float16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
     else if constexpr (EPI == 2) epilogue_fast<__bf16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
     else if constexpr (EPI == 3) epilogue_fast<_Float16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
