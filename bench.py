@@ -104,6 +104,55 @@ def bench_adamw(args):
     print(json.dumps(out), flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's reported graphics clock (sysfs pp_dpm_sclk, the line marked '*')
+    every `period` seconds on a host thread, to put the MFMA peak in terms of the clock the
+    run actually had."""
+
+    def __init__(self, period: float = 0.02):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.samples = []
+        self.period = period
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            for line in open(self.path):
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1],
+                "samples": len(xs), "source": "sysfs pp_dpm_sclk"}
+
+
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources (name + bytes, sorted): ties recorded counters to a build."""
     import hashlib
@@ -248,6 +297,8 @@ def main():
             ops.hybrid_step(list(zip(Ws, Gs, Ms)), vectors,
                             muon=dict(variant=variant_code, workspace=ws, **steps_kw), adamw=ADAMW_KW)
 
+    per_step_ms = []
+
     def timed(variant_code, steps, warmup, with_kernel_timing):
         for _ in range(warmup):
             step(variant_code)
@@ -255,20 +306,25 @@ def main():
         if with_kernel_timing:
             ops.timing_reset()
             ops.timing_enable(True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        for _ in range(steps):
+        evs[0].record()
+        for i in range(steps):
             step(variant_code)
+            evs[i + 1].record()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         kt = None
         if with_kernel_timing:
             ops.timing_enable(False)
             kt = ops.timing_query()
+            per_step_ms[:] = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
         return dt / steps, kt
 
     main_code = ops.GRAM if args.variant == "gram" else ops.STANDARD
     log(f"timing {args.variant}: warmup {args.warmup}, steps {args.steps}")
-    sec, kt = timed(main_code, args.steps, args.warmup, True)
+    with ClockSampler() as clk:
+        sec, kt = timed(main_code, args.steps, args.warmup, True)
     # event timing adds a few microseconds per launch; report the untimed run too
     sec_plain, _ = timed(main_code, max(1, args.steps // 2), 0, False)
     log(f"{args.variant}: {sec * 1e3:.2f} ms/step (with events), {sec_plain * 1e3:.2f} ms/step plain")
@@ -320,6 +376,10 @@ def main():
     if traffic is not None:
         roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         roof["traffic_source"] = f"profiles/{tsrc}"
+    clock = clk.summary()
+    if clock and unit == "flop":
+        # the dense peak scales with the graphics clock (2.4 GHz at the published figure)
+        roof["frac_at_run_clock"] = achieved / (PEAK_MFMA_TFLOPS * clock["median_mhz"] / 2400.0)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = avg_s * 1e3
     roof["launches"] = launches
@@ -365,6 +425,9 @@ def main():
         "effective_tflops": variants[args.variant]["algorithmic_tflops"],
         "frac_bf16_peak": variants[args.variant]["frac_bf16_peak"],
         "ms_per_step_plain": sec_plain * 1e3,
+        "step_ms": {"median": sorted(per_step_ms)[len(per_step_ms) // 2], "min": min(per_step_ms),
+                    "max": max(per_step_ms)},
+        "sclk": clk.summary(),
         "variants": variants,
         "kernels": per_kind,
         "roofline": roof,
