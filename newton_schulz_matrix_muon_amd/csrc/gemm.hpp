@@ -47,7 +47,7 @@ struct GemmArgs {
   // 1 when 8-element vectors of that buffer are aligned (ld, stride and base)
   int c_vec, ct_vec, w_vec, u_vec;
   // nonzero: the typed fast epilogue applies (1: f16 out/f16 E, 2: bf16/bf16, 3: f16/bf16,
-  // 4: bf16/f16, 5: f32/f32)
+  // 4: bf16/f16, 5: f32/f32; 6, 7, 8: the weight update alone, W bf16, f16, f32)
   int fast_epi;
 };
 
@@ -398,9 +398,87 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
   }
 }
 
+// Weight-update epilogue for the last product of the Muon step (no E, C or U, c0 = 0): per
+// element W <- wd_mul W - lr (u_scale v), v = s^spow c2 acc, W of dtype WT in 16-byte vectors (row-major,
+// or transposed when the caller's matrix is m x n); bit 2 of flags[mat] marks a non-finite v.
+template <typename WT, class CFG>
+__device__ inline void epilogue_wupd(const GemmArgs& p, char* lds, f32x16 (&acc)[CFG::TM][CFG::TN],
+                                     int mat, int row0, int col0) {
+  constexpr int BN = CFG::BN, NT = CFG::NT, WTM = CFG::WTM, WTN = CFG::WTN, CP = CFG::CP;
+  constexpr int TM = CFG::TM, TN = CFG::TN, SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
+  float sc = 1.f;
+  if (p.spow) {
+    const float sb = p.svec[mat];
+    sc = p.spow == 1 ? sb : sb * sb;
+  }
+  char* Wb = reinterpret_cast<char*>(p.W) + (int64_t)mat * p.sW * sizeof(WT);
+  bool bad = false;
+  float* Cs = reinterpret_cast<float*>(lds);
+  // the same operations in the same order as the generic epilogue, so both give the same W
+  auto update = [&](int64_t wi, const float (&acc8)[8]) {
+    float w[8];
+    VecIO<WT>::load(Wb, wi, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = p.c2 * acc8[e];
+      v *= sc;
+      bad |= !__builtin_isfinite(v);
+      const float u = p.u_scale * v;
+      w[e] = p.wd_mul * w[e] - p.lr * u;
+    }
+    VecIO<WT>::store(Wb, wi, w);
+  };
+  for (int sl = 0; sl < CFG::WVM / SR; ++sl) {
+    const int srow0 = row0 + sl * SROWS;
+    if (wm / SR == sl) {
+      const int lrow0 = (wm % SR) * WTM;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int r = lrow0 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            const int c = wn * WTN + j * 32 + (lane & 31);
+            Cs[r * CP + c] = acc[i][j][rr];
+          }
+    }
+    __syncthreads();
+    if (!p.w_trans) {
+      for (int idx = tid; idx < SROWS * VPR; idx += NT) {
+        const int lr = idx / VPR, lc = (idx - lr * VPR) * 8;
+        const int r = srow0 + lr, c = col0 + lc;
+        if (r >= p.M || c >= p.N) continue;
+        const float* cs = Cs + lr * CP + lc;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(cs), b = *reinterpret_cast<const f32x4*>(cs + 4);
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        update((int64_t)r * p.ldw + c, v);
+      }
+    } else {
+      // W is the caller's m x n matrix: column c of this n x m tile is row c of W
+      for (int idx = tid; idx < BN * RVC; idx += NT) {
+        const int ci = idx & 15, ri = (idx >> 4) & 3, blk = idx >> 6;
+        const int cb = blk % (BN / 16), rb = blk / (BN / 16);
+        const int lc = cb * 16 + ci, lr = (rb * 4 + ri) * 8;
+        const int r = srow0 + lr, c = col0 + lc;
+        if (c >= p.N || r >= p.M) continue;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = Cs[(lr + e) * CP + lc];
+        update((int64_t)c * p.ldw + r, v);
+      }
+    }
+    __syncthreads();
+  }
+  if (p.flags && __builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(p.flags + mat, 4);
+}
+
 // EPI selects the epilogue at compile time: 0 = generic (any dtypes, caller buffers, weight
 // update, flags); 1..5 = the typed fast epilogue (1: f16 out / f16 E, 2: bf16 / bf16,
-// 3: f16 / bf16, 4: bf16 / f16, 5: f32 / f32).
+// 3: f16 / bf16, 4: bf16 / f16, 5: f32 / f32); 6..8 = the weight update alone (W bf16, f16,
+// f32).
 // SHAPE: 0 = rectangular product, 1 = symmetric product of n x n iterates, 2 = Gram (X X^T);
 // 1 and 2 run the same code (triangle tiles) and differ only in the kernel symbol, so that
 // profiles separate the long-K Gram products from the n x n ones.
@@ -644,7 +722,10 @@ gemm_nt_kernel(const GemmBatch gb) {
     else if constexpr (EPI == 2) epilogue_fast<__bf16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
     else if constexpr (EPI == 3) epilogue_fast<_Float16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
     else if constexpr (EPI == 4) epilogue_fast<__bf16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
-    else epilogue_fast<float, float, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 5) epilogue_fast<float, float, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
+    else if constexpr (EPI == 6) epilogue_wupd<__bf16, CFG>(p, lds, acc, mat, row0, col0);
+    else if constexpr (EPI == 7) epilogue_wupd<_Float16, CFG>(p, lds, acc, mat, row0, col0);
+    else epilogue_wupd<float, CFG>(p, lds, acc, mat, row0, col0);
     continue;
   } else {
   // A) finish v = s^spow (c2 acc + c1 E) + c0 [i == j] in registers

@@ -297,6 +297,9 @@ void launch_half(int shape, int epi, dim3 grid, dim3 block, hipStream_t s, const
     case 2: launch_epi<T, CFG, 2>(shape, grid, block, s, b); break;
     case 3: launch_epi<T, CFG, 3>(shape, grid, block, s, b); break;
     case 4: launch_epi<T, CFG, 4>(shape, grid, block, s, b); break;
+    case 6: launch_epi<T, CFG, 6>(shape, grid, block, s, b); break;
+    case 7: launch_epi<T, CFG, 7>(shape, grid, block, s, b); break;
+    case 8: launch_epi<T, CFG, 8>(shape, grid, block, s, b); break;
     default: launch_epi<T, CFG, 0>(shape, grid, block, s, b); break;
   }
 }
@@ -411,6 +414,14 @@ GemmArgs gemm_args(const Prod& q, int64_t batch) {
     else if (q.c_dt == F16 && edt == BF16) a.fast_epi = 3;
     else if (q.c_dt == BF16 && edt == F16) a.fast_epi = 4;
     else if (q.c_dt == F32 && edt == F32 && q.in_dt == F32) a.fast_epi = 5;
+  }
+  // the weight update alone (the last product of the Muon step): rectangular, no E, C, C^T,
+  // U or diagonal term; W in 16-byte vectors along the direction the epilogue walks
+  if (!q.tri && q.W && !q.U && !q.C && !q.Ct && !q.E && q.c0 == 0.f && q.in_dt != F32 && a.w_vec &&
+      (q.w_trans ? q.M % 8 == 0 : q.N % 8 == 0)) {
+    if (q.w_dt == BF16) a.fast_epi = 6;
+    else if (q.w_dt == F16) a.fast_epi = 7;
+    else if (q.w_dt == F32) a.fast_epi = 8;
   }
   return a;
 }

@@ -264,3 +264,40 @@ def test_muon_step_transposed_orientation(torch, ops):
                                   nesterov=False, ns=oracle_fn("gram_stabilized"))
     assert rel_fro(to_np(Ud), Un) < 2e-2
     assert np.linalg.norm(to_np(Wd) - Wn) / np.linalg.norm(0.05 * Un) < 2e-2
+
+
+@pytest.mark.parametrize("shape,wdt", [((6, 256, 512), "bf16"), ((4, 512, 256), "bf16"), ((3, 264, 520), "f16"),
+                                       ((2, 256, 768), "f32")])
+def test_muon_step_weight_update_without_u_out(torch, ops, shape, wdt):
+    """Without U_out the last product updates W in its own epilogue; it must agree with the
+    path that also writes U (to one unit in the last place of W) and flag non-finite outputs."""
+    say(f"case muon_step W update without U_out {shape} {wdt}")
+    B, r, c = shape
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wdt]
+    G = synth.torch_lowrank_plus_noise(B, r, c, power=0.7, noise=0.05, workload_index=1,
+                                       seed_offset=31, device="cuda").to(dt if wdt != "f32" else torch.bfloat16)
+    W0 = synth.torch_weights(B, r, c, workload_index=1, device="cuda", dtype=dt)
+    kw = dict(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, scale_coeff=0.2, variant=ops.GRAM)
+    W1, W2 = W0.clone(), W0.clone()
+    M1 = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    M2 = M1.clone()
+    U = torch.empty(shape, dtype=torch.float32, device="cuda")
+    ops.muon_step(W1, G, M1, U_out=U, **kw)
+    ops.muon_step(W2, G, M2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(M1, M2)
+    a, b, w0, u = (t.double().cpu().numpy() for t in (W1, W2, W0, U))
+    # both paths evaluate the same expressions; the compiler may contract them into fused
+    # multiply-adds differently, which moves the fp32 result by a few roundings of its operands
+    # and the stored W by at most one unit in its last place
+    mant = {"bf16": 7, "f16": 10, "f32": 23}[wdt]
+    e = np.floor(np.log2(np.maximum(np.maximum(np.abs(a), np.abs(b)), 2.0 ** -14)))
+    tol = 2.0 ** (e - mant) + 4 * 2.0 ** -24 * ((1 - 0.02 * 0.1) * np.abs(w0) + 0.02 * np.abs(u))
+    assert np.all(np.abs(a - b) <= tol), float(np.max(np.abs(a - b) / tol))
+    # a NaN in one gradient: that matrix's flags report the non-finite output
+    G[1, 3, 5] = float("nan")
+    flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ops.muon_step(W2, G, M2, flags=flags, **kw)
+    torch.cuda.synchronize()
+    f = flags.cpu().tolist()
+    assert f[1] & 4 and f[1] & 1 and f[0] == 0
