@@ -1,9 +1,10 @@
 // HBM-bound kernels around the products:
 //  - prep_kernel: reads one 64 x 64 tile of a caller matrix (any dtype/ld/stride), writes it
-//    to the two internal copies the products read (X: n x m row-major, and X^T: m x n
-//    row-major), zero-fills their padded columns, and emits a deterministic per-tile partial
-//    of sum x^2 (the Frobenius norm, guide's normalisation). With momentum enabled it first
-//    applies the Muon momentum rule to the fp32 buffer M and orthogonalizes N instead of G.
+//    to the internal n x m row-major X the products read (a straight copy, or the transpose
+//    when the caller's matrix is m x n), zero-fills its padded columns, and emits a
+//    deterministic per-tile partial of sum x^2 (the Frobenius norm, guide's normalisation).
+//    With momentum enabled it first applies the Muon momentum rule to the fp32 buffer M and
+//    orthogonalizes N instead of G.
 //  - finalize_kernel: sums the partials of one matrix in a fixed order, s = 1/(sqrt + eps),
 //    and writes the per-matrix flags.
 //  - cast_kernel: dtype conversion of an n x ld internal matrix.
@@ -16,8 +17,8 @@ namespace mns {
 struct PrepArgs {
   const void* G; int g_dt; int64_t ldg, sg;
   int rows, cols;                      // caller orientation
-  void* out_same; int64_t ld_same, s_same;   // rows x ld_same (pad cols zero)
-  void* out_tr; int64_t ld_tr, s_tr;         // cols x ld_tr   (pad cols zero)
+  void* out_same; int64_t ld_same, s_same;   // rows x ld_same (pad cols zero), or null
+  void* out_tr; int64_t ld_tr, s_tr;         // cols x ld_tr   (pad cols zero), or null
   int io_dt;
   double* partials;                    // [batch][tiles]
   int tiles_x, tiles;                  // tiles_x = ceil(cols/64)
@@ -38,8 +39,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
   const int es = dtype_size(p.g_dt), ios = dtype_size(p.io_dt);
   const char* Gb = reinterpret_cast<const char*>(p.G) + (int64_t)mat * p.sg * es;
   float* Mb = p.M ? p.M + (int64_t)mat * p.sm : nullptr;
-  char* Sb = reinterpret_cast<char*>(p.out_same) + (int64_t)mat * p.s_same * ios;
-  char* Tb = reinterpret_cast<char*>(p.out_tr) + (int64_t)mat * p.s_tr * ios;
+  char* Sb = p.out_same ? reinterpret_cast<char*>(p.out_same) + (int64_t)mat * p.s_same * ios : nullptr;
+  char* Tb = p.out_tr ? reinterpret_cast<char*>(p.out_tr) + (int64_t)mat * p.s_tr * ios : nullptr;
 
   // load: thread -> 4 consecutive columns of rows ty + 16q
   const int cc = (tid & 15) * 4, rbase = tid >> 4;
@@ -72,7 +73,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int lr = rbase + 16 * q, r = r0 + lr;
-    if (r >= p.rows) continue;
+    if (!Sb || r >= p.rows) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int c = c0 + cc + e;
@@ -83,7 +84,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int lc = rbase + 16 * q, c = c0 + lc;
-    if (c >= p.cols) continue;
+    if (!Tb || c >= p.cols) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + cc + e;
@@ -156,8 +157,8 @@ __global__ void __launch_bounds__(256) prep_vec_kernel(const PrepArgs p) {
   const int r0 = ty * PREP_T, c0 = tx * PREP_T;
   const T* Gb = reinterpret_cast<const T*>(p.G) + (int64_t)mat * p.sg;
   float* Mb = p.M ? p.M + (int64_t)mat * p.sm : nullptr;
-  T* Sb = reinterpret_cast<T*>(p.out_same) + (int64_t)mat * p.s_same;
-  T* Tb = reinterpret_cast<T*>(p.out_tr) + (int64_t)mat * p.s_tr;
+  T* Sb = p.out_same ? reinterpret_cast<T*>(p.out_same) + (int64_t)mat * p.s_same : nullptr;
+  T* Tb = p.out_tr ? reinterpret_cast<T*>(p.out_tr) + (int64_t)mat * p.s_tr : nullptr;
   // thread -> rows (tid >> 3) and (tid >> 3) + 32, columns 8 (tid & 7) .. + 7
   const int cv = (tid & 7) * 8;
   double ss = 0.0;
@@ -188,16 +189,18 @@ __global__ void __launch_bounds__(256) prep_vec_kernel(const PrepArgs p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.f;
     }
-    if (r < p.rows && c < p.ld_same) st8<T>(Sb + (int64_t)r * p.ld_same + c, v);
+    if (Sb && r < p.rows && c < p.ld_same) st8<T>(Sb + (int64_t)r * p.ld_same + c, v);
+    if (Tb) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tile[lr][cv + e] = v[e];
+      for (int e = 0; e < 8; ++e) tile[lr][cv + e] = v[e];
+    }
   }
   __syncthreads();
   // transposed: thread -> tile column (tid >> 3) and +32, rows 8 (tid & 7) .. + 7
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int lc = (tid >> 3) + 32 * h, c = c0 + lc, r = r0 + cv;
-    if (c < p.cols && r < p.ld_tr) {
+    if (Tb && c < p.cols && r < p.ld_tr) {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = tile[cv + e][lc];

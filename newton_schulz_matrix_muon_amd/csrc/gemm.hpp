@@ -1,13 +1,14 @@
 // Batched "NT" matrix product on MFMA for gfx950, with the Newton-Schulz epilogues fused.
 //
-//   C[b][i][j] = sum_k A[b][i][k] * B[b][j][k]     (both operands K-contiguous)
+//   C[b][i][j] = sum_k A[b][i][k] * B[b][j][k]     (A K-contiguous; B K-contiguous, or
+//                                                   stored k-major as B[b][k][j])
 //
 // Every product of the method has this form:
 //  - X X^T (the Gram / SYRK product): A = B = X (n x m, row-major), K = m;
 //  - products of the symmetric n x n iterates (R R, R Z, Z (R Z), Z Q, A A): the right
 //    operand is symmetric and stored in full, so its rows are its columns;
-//  - the rectangular Q X and B X: the right operand is X^T, kept as an (m x n) row-major
-//    copy whose rows are the columns of X.
+//  - the rectangular Q X and B X: the right operand is X itself (n x m row-major), read
+//    k-major through gfx950's transposing LDS reads, so no transposed copy of X exists.
 // TRI=true computes only the tiles on or above the diagonal of a symmetric result and
 // writes each value to (i, j) and (j, i), so stored symmetric matrices are exactly
 // symmetric.
@@ -210,7 +211,7 @@ template <> struct VecIO<_Float16> : VecIO16<_Float16> {};
 template <typename T> struct Frag { typedef T type __attribute__((ext_vector_type(8))); };
 template <> struct Frag<float> { typedef f32x4 type; };
 
-template <typename T, int TM, int TN, int ROWB>
+template <typename T, int TM, int TN, int ROWB, bool LB = true>
 __device__ inline void load_frags(const char* As, const char* Bs, int lane, int g,
                                   typename Frag<T>::type (&a)[TM], typename Frag<T>::type (&b)[TN]) {
   typedef typename Frag<T>::type F;
@@ -218,8 +219,10 @@ __device__ inline void load_frags(const char* As, const char* Bs, int lane, int 
   const int off = g * 32 + hi * 16;
 #pragma unroll
   for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const F*>(As + (i * 32 + l32) * ROWB + off);
+  if constexpr (LB) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * ROWB + off);
+    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * ROWB + off);
+  }
 }
 
 // XOR swizzle of the 16-byte chunk index within an unpadded k-stage row, as a function of the
@@ -230,7 +233,7 @@ __device__ __host__ constexpr int chunk_swizzle(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-template <typename T, int TM, int TN, int KB>
+template <typename T, int TM, int TN, int KB, bool LB = true>
 __device__ inline void load_frags_dl(const char* As, const char* Bs, int lane, int g, int sw,
                                      typename Frag<T>::type (&a)[TM], typename Frag<T>::type (&b)[TN]) {
   typedef typename Frag<T>::type F;
@@ -238,8 +241,77 @@ __device__ inline void load_frags_dl(const char* As, const char* Bs, int lane, i
   const int off = (((2 * g + hi) ^ sw) << 4);
 #pragma unroll
   for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const F*>(As + (i * 32 + l32) * KB + off);
+  if constexpr (LB) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * KB + off);
+    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const F*>(Bs + (j * 32 + l32) * KB + off);
+  }
+}
+
+// B operand stored k-major (element (n, k) of the NT operand at B[k * ldb + n]: the X of a
+// rectangular product Q X read in place). A stage holds BK k-rows of BN values; its 16-byte
+// chunks are XOR-swizzled by kmajor_swizzle(k & 3), which keeps the transposing reads below
+// free of bank conflicts for 32- and 64-bank LDS (rows at least 16 chunks long).
+__device__ __host__ constexpr int kmajor_swizzle(int s) { return (4 * s) ^ (2 * (s >> 1)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Per-lane byte offset of fragment column block j (16-bit types) inside a k-major B stage of
+// RB bytes per k-row, before the k-group offset. ds_read_b64_tr_b16 hands lane i of each
+// 16-lane group element (i mod 4) of the 8-byte pieces addressed by lanes 4e + i / 4
+// (e = 0..3); addressing rows k0 + j16 / 4 at columns 16 qo + 4 (j16 mod 4) therefore gives
+// lane (qo, i) the values B[k0 + e][16 qo + i], four consecutive k of one column.
+template <int RB>
+__device__ inline int kmajor_frag_off(int lane, int n0) {
+  const int j16 = lane & 15, qo = (lane >> 4) & 1, hi = lane >> 5;
+  const int n = n0 + 16 * qo + 4 * (j16 & 3);
+  return (8 * hi + (j16 >> 2)) * RB + (((n >> 3) ^ kmajor_swizzle(j16 >> 2)) << 4) + 8 * (j16 & 1);
+}
+
+// B fragments (8 consecutive k of one column per lane, the layout load_frags gives) from a
+// k-major stage: two transposing 8-byte reads per fragment (k 0..3 and 4..7 of the lane's
+// half of the 16-wide k-group g).
+//
+// The reads are issued from inline assembly that also waits for them: the compiler treats
+// the transposing-read builtin as possibly reading what the in-flight global -> LDS DMA of
+// the next k-stage writes and would wait for that DMA before every read, serialising the
+// DMA with the MFMAs. The DMA ring's own waits and barriers order these reads correctly.
+template <typename T, int TN, int RB>
+__device__ inline void load_b_kmajor(const char* Bs, const int (&boff)[TN], int g,
+                                     typename Frag<T>::type (&b)[TN]) {
+  typedef typename Frag<T>::type F;
+  typedef __attribute__((address_space(3))) const char* lds_ptr;
+  static_assert(TN == 2, "two column blocks per wave");
+  const unsigned a0 = (unsigned)(size_t)(lds_ptr)(Bs + boff[0] + 16 * g * RB);
+  const unsigned a1 = (unsigned)(size_t)(lds_ptr)(Bs + boff[1] + 16 * g * RB);
+  s16x4 lo0, hi0, lo1, hi1;
+  __asm__ __volatile__(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1)
+      : "v"(a0), "v"(a1), "i"(4 * RB)
+      : "memory");
+  b[0] = __builtin_bit_cast(F, (s16x8)__builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7));
+  b[1] = __builtin_bit_cast(F, (s16x8)__builtin_shufflevector(lo1, hi1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// fp32 B fragments from a k-major stage (lane (l32, hi) holds k = 8 g + 4 hi + e of column
+// n0 + l32): four 4-byte reads; consecutive lanes read consecutive columns.
+template <int TN, int RB>
+__device__ inline void load_b_kmajor_f32(const char* Bs, int lane, int n0, int g, f32x4 (&b)[TN]) {
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + j * 32 + l32;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 8 * g + 4 * hi + e;
+      b[j][e] = *reinterpret_cast<const float*>(Bs + k * RB + (((n >> 2) ^ kmajor_swizzle(e)) << 4) + (n & 3) * 4);
+    }
+  }
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt low/high bits, expcnt
@@ -479,13 +551,15 @@ __device__ inline void epilogue_wupd(const GemmArgs& p, char* lds, f32x16 (&acc)
 // update, flags); 1..5 = the typed fast epilogue (1: f16 out / f16 E, 2: bf16 / bf16,
 // 3: f16 / bf16, 4: bf16 / f16, 5: f32 / f32); 6..8 = the weight update alone (W bf16, f16,
 // f32).
-// SHAPE: 0 = rectangular product, 1 = symmetric product of n x n iterates, 2 = Gram (X X^T);
-// 1 and 2 run the same code (triangle tiles) and differ only in the kernel symbol, so that
-// profiles separate the long-K Gram products from the n x n ones.
+// SHAPE: 0 = full product (both operands K-contiguous), 1 = symmetric product of n x n
+// iterates, 2 = Gram (X X^T), 3 = rectangular product with the k-major right operand (Q X,
+// B X); 1 and 2 run the same code (triangle tiles) and differ only in the kernel symbol, so
+// that profiles separate the long-K Gram products from the n x n ones.
 template <typename T, int SHAPE, class CFG, int EPI>
 __global__ void __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::OCC, CFG::OCC)))
 gemm_nt_kernel(const GemmBatch gb) {
-  constexpr bool TRI = SHAPE != 0;
+  constexpr bool TRI = SHAPE == 1 || SHAPE == 2;
+  constexpr bool BKM = SHAPE == 3;
   constexpr int ES = MfmaTraits<T>::ES;
   constexpr int EPC = 16 / ES;     // elements per 16-byte chunk
   constexpr int BK = CFG::CPR * EPC;  // elements of K per stage
@@ -539,7 +613,7 @@ gemm_nt_kernel(const GemmBatch gb) {
   const char* Ab = reinterpret_cast<const char*>(p.A) + (int64_t)mat * p.sA * ES;
   const char* Bb = reinterpret_cast<const char*>(p.B) + (int64_t)mat * p.sB * ES;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Ab, (uint32_t)((int64_t)p.M * p.lda * ES));
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bb, (uint32_t)((int64_t)p.N * p.ldb * ES));
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bb, (uint32_t)((int64_t)(BKM ? p.K : p.N) * p.ldb * ES));
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -564,17 +638,27 @@ gemm_nt_kernel(const GemmBatch gb) {
     int ldsoff[D];
     bool isA[D];
     const int rib = lane / CPR, pch = lane % CPR;
+    // k-major B: a 1 KB block is KRB k-rows of BN values (CPK chunks each)
+    constexpr int CPK = BN * ES / 16, KRB = 1024 / (BN * ES);
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int blk = wave * D + j;
       isA[j] = blk < NBA;
-      const int lrow = (isA[j] ? blk : blk - NBA) * RPB + rib;   // tile-local row
-      const int logical = pch ^ chunk_swizzle<CPR>(lrow);
-      const int grow = (isA[j] ? row0 : col0) + lrow;
-      const int lim = isA[j] ? p.M : p.N;
-      const int64_t ld = isA[j] ? p.lda : p.ldb;
-      goff[j] = grow < lim ? (uint32_t)(grow * ld * ES + logical * 16) : OOB;
-      kchunk[j] = logical * EPC;
+      if (BKM && !isA[j]) {
+        const int krow = (blk - NBA) * KRB + lane / CPK;
+        const int logical = (lane % CPK) ^ kmajor_swizzle(krow & 3);
+        const int gcol = col0 + logical * EPC;
+        goff[j] = gcol < p.N ? (uint32_t)(krow * p.ldb * ES + gcol * ES) : OOB;
+        kchunk[j] = krow;
+      } else {
+        const int lrow = (isA[j] ? blk : blk - NBA) * RPB + rib;   // tile-local row
+        const int logical = pch ^ chunk_swizzle<CPR>(lrow);
+        const int grow = (isA[j] ? row0 : col0) + lrow;
+        const int lim = isA[j] ? p.M : p.N;
+        const int64_t ld = isA[j] ? p.lda : p.ldb;
+        goff[j] = grow < lim ? (uint32_t)(grow * ld * ES + logical * 16) : OOB;
+        kchunk[j] = logical * EPC;
+      }
       ldsoff[j] = isA[j] ? blk * 1024 : BM * KB + (blk - NBA) * 1024;
     }
     const int nk = (p.K + BK - 1) / BK;
@@ -583,7 +667,11 @@ gemm_nt_kernel(const GemmBatch gb) {
       const int k0 = ks * BK;
 #pragma unroll
       for (int j = 0; j < D; ++j) {
-        const uint32_t off = (k0 + kchunk[j] < p.K) ? goff[j] + (uint32_t)(k0 * ES) : OOB;
+        uint32_t off;
+        if constexpr (BKM)  // k-major B advances by whole rows of ldb elements per unit of k
+          off = (k0 + kchunk[j] < p.K) ? goff[j] + (uint32_t)k0 * (isA[j] ? (uint32_t)ES : (uint32_t)(p.ldb * ES)) : OOB;
+        else
+          off = (k0 + kchunk[j] < p.K) ? goff[j] + (uint32_t)(k0 * ES) : OOB;
         dma16(isA[j] ? rsA : rsB, sb + ldsoff[j], off);
       }
     };
@@ -597,6 +685,9 @@ gemm_nt_kernel(const GemmBatch gb) {
     const int sw = chunk_swizzle<CPR>(lane & 31);
     typedef typename Frag<T>::type F;
     F fa[TM], fb[TN];
+    int boff[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) boff[j] = BKM ? kmajor_frag_off<BN * ES>(lane, wn * WTN + j * 32) : 0;
 #pragma unroll
     for (int s_ = 0; s_ < PD; ++s_)
       if (s_ < nk) issue(s_);
@@ -609,7 +700,15 @@ gemm_nt_kernel(const GemmBatch gb) {
       const char* Bs = sb + (BM + wn * WTN) * KB;
 #pragma unroll
       for (int g = 0; g < CFG::NG; ++g) {
-        load_frags_dl<T, TM, TN, KB>(As, Bs, lane, g, sw, fa, fb);
+        if constexpr (BKM && ES == 2) {
+          load_frags_dl<T, TM, TN, KB, false>(As, Bs, lane, g, sw, fa, fb);
+          load_b_kmajor<T, TN, BN * ES>(sb + BM * KB, boff, g, fb);
+        } else if constexpr (BKM) {
+          load_frags_dl<T, TM, TN, KB, false>(As, Bs, lane, g, sw, fa, fb);
+          load_b_kmajor_f32<TN, BN * ES>(sb + BM * KB, lane, wn * WTN, g, fb);
+        } else {
+          load_frags_dl<T, TM, TN, KB>(As, Bs, lane, g, sw, fa, fb);
+        }
         mma<T, TM, TN>(fa, fb, acc);
       }
       // stage kt + 1 must have landed; stages kt + 2 .. min(kt + PD, nk - 1) may be in flight
@@ -627,12 +726,23 @@ gemm_nt_kernel(const GemmBatch gb) {
     const int c = tid + NT * q, ga = row0 + c / CPR;
     offA[q] = ga < p.M ? (uint32_t)(ga * p.lda * ES + (c % CPR) * 16) : OOB;
   }
+  // k-major B: chunk c is logical chunk c % CPK of k-row c / CPK, stored swizzled
+  constexpr int CPK = BN * ES / 16;
+  int krowB[CFG::CB];
 #pragma unroll
   for (int q = 0; q < CFG::CB; ++q) {
-    const int c = tid + NT * q, gb = col0 + c / CPR;
-    offB[q] = gb < p.N ? (uint32_t)(gb * p.ldb * ES + (c % CPR) * 16) : OOB;
+    const int c = tid + NT * q;
+    if constexpr (BKM) {
+      const int gcol = col0 + (c % CPK) * EPC;
+      krowB[q] = c / CPK;
+      offB[q] = gcol < p.N ? (uint32_t)(krowB[q] * p.ldb * ES + gcol * ES) : OOB;
+    } else {
+      const int gb = col0 + c / CPR;
+      krowB[q] = 0;
+      offB[q] = gb < p.N ? (uint32_t)(gb * p.ldb * ES + (c % CPR) * 16) : OOB;
+    }
   }
-  const int kc = (tid % CPR) * EPC;  // k offset of this thread's chunks within a stage
+  const int kc = (tid % CPR) * EPC;  // k offset of this thread's A (and row-major B) chunks
   u32x4 ra[PF][CFG::CA], rb[PF][CFG::CB];
   const int nk = (p.K + BK - 1) / BK;
 
@@ -642,9 +752,16 @@ gemm_nt_kernel(const GemmBatch gb) {
 #pragma unroll
     for (int q = 0; q < CFG::CA; ++q)
       ra[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rsA, kin ? offA[q] + kb : OOB, 0, 0);
+    if constexpr (BKM) {
+      const uint32_t kbB = (uint32_t)k0 * (uint32_t)(p.ldb * ES);
 #pragma unroll
-    for (int q = 0; q < CFG::CB; ++q)
-      rb[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rsB, kin ? offB[q] + kb : OOB, 0, 0);
+      for (int q = 0; q < CFG::CB; ++q)
+        rb[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rsB, k0 + krowB[q] < p.K ? offB[q] + kbB : OOB, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < CFG::CB; ++q)
+        rb[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rsB, kin ? offB[q] + kb : OOB, 0, 0);
+    }
   };
   auto store_stage = [&](int buf, int set) {
     char* As_ = lds + buf * CFG::STAGE;
@@ -657,13 +774,19 @@ gemm_nt_kernel(const GemmBatch gb) {
 #pragma unroll
     for (int q = 0; q < CFG::CB; ++q) {
       const int c = tid + NT * q;
-      *reinterpret_cast<u32x4*>(Bs_ + (c / CPR) * ROWB + (c % CPR) * 16) = rb[set][q];
+      if constexpr (BKM)
+        *reinterpret_cast<u32x4*>(Bs_ + krowB[q] * (BN * ES) + (((c % CPK) ^ kmajor_swizzle(krowB[q] & 3)) << 4)) = rb[set][q];
+      else
+        *reinterpret_cast<u32x4*>(Bs_ + (c / CPR) * ROWB + (c % CPR) * 16) = rb[set][q];
     }
   };
 
 
   typedef typename Frag<T>::type F;
   F fa[TM], fb[TN];
+  int boff[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) boff[j] = BKM ? kmajor_frag_off<BN * ES>(lane, wn * WTN + j * 32) : 0;
   // Prologue: stage 0 in LDS, stages 1 .. PF-1 in flight in register sets 1 .. PF-1.
 #pragma unroll
   for (int s_ = 0; s_ < PF; ++s_)
@@ -685,7 +808,15 @@ gemm_nt_kernel(const GemmBatch gb) {
     // one fragment set: the other waves of the SIMD cover the LDS latency
 #pragma unroll
     for (int g = 0; g < CFG::NG; ++g) {
-      load_frags<T, TM, TN, ROWB>(As, Bs, lane, g, fa, fb);
+      if constexpr (BKM && ES == 2) {
+        load_frags<T, TM, TN, ROWB, false>(As, Bs, lane, g, fa, fb);
+        load_b_kmajor<T, TN, BN * ES>(lds + cur * CFG::STAGE + BM * ROWB, boff, g, fb);
+      } else if constexpr (BKM) {
+        load_frags<T, TM, TN, ROWB, false>(As, Bs, lane, g, fa, fb);
+        load_b_kmajor_f32<TN, BN * ES>(lds + cur * CFG::STAGE + BM * ROWB, lane, wn * WTN, g, fb);
+      } else {
+        load_frags<T, TM, TN, ROWB>(As, Bs, lane, g, fa, fb);
+      }
       mma<T, TM, TN>(fa, fb, acc);
     }
     if (kt + 1 < nk) store_stage(cur ^ 1, nset);

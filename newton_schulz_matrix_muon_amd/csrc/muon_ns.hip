@@ -178,7 +178,7 @@ struct Buf {
 
 struct Layout {
   size_t total = 0;
-  Buf svec, partials, X0, Xt0, Xt1, X1, A, Bm, R, Z, W, Qa, Qb;
+  Buf svec, partials, X0, X1, A, Bm, R, Z, W, Qa, Qb;
 };
 
 // Restart bits that take effect: steps k = 1 .. K-1 (bit k).
@@ -205,16 +205,16 @@ Layout plan(int variant, const Geo& g, const NsConf& c, int64_t chunk) {
   const int qdt = dtype_size(io) >= dtype_size(it) ? io : it;
   add(L.svec, 1, 4, true);
   add(L.partials, g.prep_tiles, 8, true);
+  // X (n x ldm, row-major) is the only copy of an iterate: the rectangular products read it
+  // k-major as their B operand, so no transposed copy is kept
   add(L.X0, (int64_t)g.n * g.ldm, io);
-  add(L.Xt0, (int64_t)g.m * g.ldn, io);
   const int64_t nn = (int64_t)g.n * g.ldn;
   if (variant == MNS_VARIANT_STANDARD) {
     add(L.X1, (int64_t)g.n * g.ldm, io);
-    add(L.Xt1, (int64_t)g.m * g.ldn, io);
     add(L.A, nn, it);
     add(L.Bm, nn, dtype_size(io) >= dtype_size(it) ? io : it);
   } else {
-    if (restarts_used(c)) add(L.Xt1, (int64_t)g.m * g.ldn, io);
+    if (restarts_used(c)) add(L.X1, (int64_t)g.n * g.ldm, io);
     add(L.R, nn, it);
     add(L.Z, nn, it);
     add(L.W, nn, it);
@@ -246,6 +246,7 @@ struct Prod {
   const void* B = nullptr; int64_t ldb = 0, sB = 0;
   int M = 0, N = 0, K = 0, in_dt = 0;
   bool tri = false;
+  bool bkm = false;  // B stored k-major: element (n, k) at B[k * ldb + n]
   const float* svec = nullptr; int spow = 0;
   float c0 = 0.f, c1 = 0.f, c2 = 1.f;
   const void* E = nullptr; int e_dt = 0; int64_t lde = 0, sE = 0; int e_rows = 0, e_cols = 0;
@@ -285,7 +286,8 @@ int resident_slots() {
 
 template <typename T, class CFG, int EPI>
 void launch_epi(int shape, dim3 grid, dim3 block, hipStream_t s, const GemmBatch& b) {
-  if (shape == 2) hipLaunchKernelGGL((gemm_nt_kernel<T, 2, CFG, EPI>), grid, block, 0, s, b);
+  if (shape == 3) hipLaunchKernelGGL((gemm_nt_kernel<T, 3, CFG, EPI>), grid, block, 0, s, b);
+  else if (shape == 2) hipLaunchKernelGGL((gemm_nt_kernel<T, 2, CFG, EPI>), grid, block, 0, s, b);
   else if (shape == 1) hipLaunchKernelGGL((gemm_nt_kernel<T, 1, CFG, EPI>), grid, block, 0, s, b);
   else hipLaunchKernelGGL((gemm_nt_kernel<T, 0, CFG, EPI>), grid, block, 0, s, b);
 }
@@ -351,7 +353,7 @@ int launch_prod(const Prod* qs, const GemmArgs* as, const int64_t* batches, int 
   const int fast = as[0].fast_epi;
   const int64_t per_xcd = fast ? std::min<int64_t>(xmax, std::max(1, resident_slots<CFG>() / 8)) : xmax;
   dim3 grid((unsigned)(8 * std::max<int64_t>(1, per_xcd))), block(CFG::NT);
-  const int shape = !qs[0].tri ? 0 : (kind == K_SYRK ? 2 : 1);
+  const int shape = !qs[0].tri ? (qs[0].bkm ? 3 : 0) : (kind == K_SYRK ? 2 : 1);
   const int in_dt = qs[0].in_dt;
   return launch(kind, s, [&] {
     if (in_dt == F32) {
@@ -434,9 +436,16 @@ int run_prods(const Prod* qs, const int64_t* batches, int ng, int kind, hipStrea
   int tc[MNS_MAXG];
   bool same = true;
   for (int i = 0; i < ng; ++i) {
-    as[i] = gemm_args(qs[i], batches[i]);
-    tc[i] = tile_choice(qs[i], batches[i]);
-    if (i && (qs[i].in_dt != qs[0].in_dt || qs[i].tri != qs[0].tri ||
+    const Prod& q = qs[i];
+    // the kernels address one operand matrix with 32-bit byte offsets and use offsets from
+    // 2^31 up as the zero-fill sentinel: each operand matrix must span at most 2^31 bytes
+    const int64_t es = dtype_size(q.in_dt);
+    if ((int64_t)q.M * q.lda * es > (int64_t(1) << 31) ||
+        (int64_t)(q.bkm ? q.K : q.N) * q.ldb * es > (int64_t(1) << 31))
+      return MNS_ERR_SHAPE;
+    as[i] = gemm_args(q, batches[i]);
+    tc[i] = tile_choice(q, batches[i]);
+    if (i && (q.in_dt != qs[0].in_dt || q.tri != qs[0].tri || q.bkm != qs[0].bkm ||
               as[i].fast_epi != as[0].fast_epi || tc[i] != tc[0]))
       same = false;
   }
@@ -516,20 +525,18 @@ Prod gram_prod(const void* X, int io_dt, const Geo& g, void* C, int c_dt, const 
   return q;
 }
 
-// Rectangular C = L . X for an n x n L and X given by its (m x ldn) transposed copy.
-Prod rect_prod(const void* L, const void* Xt, int io_dt, const Geo& g) {
+// Rectangular C = L . X for an n x n L and the n x m row-major X, read k-major in place.
+Prod rect_prod(const void* L, const void* X, int io_dt, const Geo& g) {
   Prod q;
   q.A = L; q.lda = g.ldn; q.sA = (int64_t)g.n * g.ldn;
-  q.B = Xt; q.ldb = g.ldn; q.sB = (int64_t)g.m * g.ldn;
+  q.B = X; q.ldb = g.ldm; q.sB = (int64_t)g.n * g.ldm; q.bkm = true;
   q.M = g.n; q.N = g.m; q.K = g.n; q.in_dt = io_dt; q.tri = false;
   return q;
 }
 
-void set_internal_x_out(Prod& q, void* X, void* Xt, int x_dt, const Geo& g) {
+void set_internal_x_out(Prod& q, void* X, int x_dt, const Geo& g) {
   q.C = X; q.c_dt = x_dt; q.ldc = g.ldm; q.sC = (int64_t)g.n * g.ldm;
   q.c_rows = g.n; q.c_cols = (int)g.ldm;
-  q.Ct = Xt; q.ct_dt = x_dt; q.ldct = g.ldn; q.sCt = (int64_t)g.m * g.ldn;
-  q.ct_rows = g.m; q.ct_cols = (int)g.ldn;
 }
 
 struct Source {
@@ -547,13 +554,13 @@ int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, 
   a.G = reinterpret_cast<const char*>(G->ptr) + b0 * G->stride * es;
   a.g_dt = G->dtype; a.ldg = G->ld; a.sg = G->stride;
   a.rows = (int)G->rows; a.cols = (int)G->cols;
+  // X0 = G in the n x m orientation: a straight copy, or the transpose of an m x n G
   void* X0 = at<char>(ws, L.X0);
-  void* Xt0 = at<char>(ws, L.Xt0);
+  a.out_same = nullptr; a.ld_same = 0; a.s_same = 0;
+  a.out_tr = nullptr; a.ld_tr = 0; a.s_tr = 0;
   if (!g.trans) {
     a.out_same = X0; a.ld_same = g.ldm; a.s_same = (int64_t)g.n * g.ldm;
-    a.out_tr = Xt0; a.ld_tr = g.ldn; a.s_tr = (int64_t)g.m * g.ldn;
   } else {
-    a.out_same = Xt0; a.ld_same = g.ldn; a.s_same = (int64_t)g.m * g.ldn;
     a.out_tr = X0; a.ld_tr = g.ldm; a.s_tr = (int64_t)g.n * g.ldm;
   }
   a.io_dt = c.io_dt;
@@ -614,12 +621,12 @@ int run_all(const Part* P, int np, int kind, hipStream_t s, F&& make) {
 
 int run_standard(const Part* P, int np, const NsConf& c, hipStream_t s) {
   const int io = c.io_dt, it = c.it_dt;
-  struct Bufs { const float* sv; char* X[2]; char* Xt[2]; char* A; char* Bm; } B[MNS_MAXG];
+  struct Bufs { const float* sv; char* X[2]; char* A; char* Bm; } B[MNS_MAXG];
   for (int i = 0; i < np; ++i) {
     const Layout& L = P[i].L;
     void* ws = P[i].ws;
-    B[i] = {at<float>(ws, L.svec), {at<char>(ws, L.X0), at<char>(ws, L.X1)},
-            {at<char>(ws, L.Xt0), at<char>(ws, L.Xt1)}, at<char>(ws, L.A), at<char>(ws, L.Bm)};
+    B[i] = {at<float>(ws, L.svec), {at<char>(ws, L.X0), at<char>(ws, L.X1)}, at<char>(ws, L.A),
+            at<char>(ws, L.Bm)};
   }
   int cur = 0;
   // X0 is the caller's values in the input dtype; every later X_k is normalised and is
@@ -644,12 +651,12 @@ int run_standard(const Part* P, int np, const NsConf& c, hipStream_t s) {
     // X <- s (a X + B X)
     if (int st = run_all(P, np, K_RECT, s, [&](int i) {
           const Geo& g = P[i].g;
-          Prod q = rect_prod(B[i].Bm, B[i].Xt[cur], xdt, g);
+          Prod q = rect_prod(B[i].Bm, B[i].X[cur], xdt, g);
           q.svec = B[i].sv; q.spow = first ? 1 : 0;
           q.c1 = a_k; q.c2 = 1.f;
           q.E = B[i].X[cur]; q.e_dt = xdt; q.lde = g.ldm; q.sE = (int64_t)g.n * g.ldm; q.e_rows = g.n;
           q.e_cols = (int)g.ldm;
-          if (k < c.steps) set_internal_x_out(q, B[i].X[cur ^ 1], B[i].Xt[cur ^ 1], it, g);
+          if (k < c.steps) set_internal_x_out(q, B[i].X[cur ^ 1], it, g);
           else set_final(q, P[i].fo, g, P[i].b0);
           return q;
         })) return st;
@@ -673,21 +680,22 @@ int trace_copy(const char* R, int it, const Geo& g, float* dst, hipStream_t s) {
 
 int run_gram(const Part* P, int np, const NsConf& c, hipStream_t s, float* trace = nullptr) {
   const int io = c.io_dt, it = c.it_dt;
-  struct Bufs { const float* sv; char* Xrow; char* Xtb[2]; char* R; char* Z; char* Wb; char* Qbuf[2]; } B[MNS_MAXG];
+  struct Bufs { const float* sv; char* X[2]; char* R; char* Z; char* Wb; char* Qbuf[2]; } B[MNS_MAXG];
   for (int i = 0; i < np; ++i) {
     const Layout& L = P[i].L;
     void* ws = P[i].ws;
-    B[i] = {at<float>(ws, L.svec), at<char>(ws, L.X0),            // X: n x ldm, overwritten at restarts
-            {at<char>(ws, L.Xt0), L.Xt1.per ? at<char>(ws, L.Xt1) : nullptr},
+    // X: n x ldm; a restart writes Q X into the other buffer (every output tile reads whole
+    // columns of X, so the product cannot run in place)
+    B[i] = {at<float>(ws, L.svec), {at<char>(ws, L.X0), L.X1.per ? at<char>(ws, L.X1) : nullptr},
             at<char>(ws, L.R), at<char>(ws, L.Z), at<char>(ws, L.W),
             {at<char>(ws, L.Qa), at<char>(ws, L.Qb)}};
   }
-  int xt = 0;
+  int xc = 0;
   int xspow = 1;  // the current X is the unnormalised input: scale by s once
   int xdt = io;   // dtype of the current X; normalised restarts store it in the iterate dtype
 
   if (int st = run_all(P, np, K_SYRK, s, [&](int i) {
-        return gram_prod(B[i].Xrow, xdt, P[i].g, B[i].R, it, B[i].sv, 2);
+        return gram_prod(B[i].X[xc], xdt, P[i].g, B[i].R, it, B[i].sv, 2);
       })) return st;
 
   bool q_fresh = true;
@@ -727,16 +735,16 @@ int run_gram(const Part* P, int np, const NsConf& c, hipStream_t s, float* trace
     if (restart) {
       // X <- Q X (explicit), R <- X X^T, Q <- I
       if (int st = run_all(P, np, K_RECT, s, [&](int i) {
-            Prod q = rect_prod(B[i].Qbuf[qcur], B[i].Xtb[xt], xdt, P[i].g);
+            Prod q = rect_prod(B[i].Qbuf[qcur], B[i].X[xc], xdt, P[i].g);
             q.svec = B[i].sv; q.spow = xspow;
-            set_internal_x_out(q, B[i].Xrow, B[i].Xtb[xt ^ 1], it, P[i].g);
+            set_internal_x_out(q, B[i].X[xc ^ 1], it, P[i].g);
             return q;
           })) return st;
-      xt ^= 1;
+      xc ^= 1;
       xspow = 0;
       xdt = it;
       if (int st = run_all(P, np, K_SYRK, s, [&](int i) {
-            return gram_prod(B[i].Xrow, xdt, P[i].g, B[i].R, it, B[i].sv, 0);
+            return gram_prod(B[i].X[xc], xdt, P[i].g, B[i].R, it, B[i].sv, 0);
           })) return st;
       q_fresh = true;
     } else if (k < c.steps) {
@@ -755,7 +763,7 @@ int run_gram(const Part* P, int np, const NsConf& c, hipStream_t s, float* trace
   }
   // output = s^xspow Q X
   return run_all(P, np, K_RECT, s, [&](int i) {
-    Prod q = rect_prod(B[i].Qbuf[qcur], B[i].Xtb[xt], xdt, P[i].g);
+    Prod q = rect_prod(B[i].Qbuf[qcur], B[i].X[xc], xdt, P[i].g);
     q.svec = B[i].sv; q.spow = xspow;
     set_final(q, P[i].fo, P[i].g, P[i].b0);
     return q;
