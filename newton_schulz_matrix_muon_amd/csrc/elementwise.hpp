@@ -216,6 +216,59 @@ __global__ void __launch_bounds__(256) prep_vec_kernel(const PrepArgs p) {
   if (tid == 0) p.partials[(int64_t)mat * p.tiles + blockIdx.x] = red[0];
 }
 
+// Streaming prep for the common case: X in the caller's orientation (rows <= cols), aligned
+// buffers, cols a multiple of 8 (so X has no padded columns). Block b of a matrix handles the
+// 512 consecutive 8-element vectors from 512 b on (two per thread, 256 apart: every wave
+// reads and writes contiguous runs), with the arithmetic of prep_vec_kernel and a fixed-order
+// reduction of its partial sum of squares.
+constexpr int PREP_SV = 512;
+
+template <typename T>
+__global__ void __launch_bounds__(256) prep_stream_kernel(const PrepArgs p) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  const int mat = blockIdx.y;
+  const int vpr = p.cols / 8;
+  const int64_t nvec = (int64_t)p.rows * vpr;
+  const T* Gb = reinterpret_cast<const T*>(p.G) + (int64_t)mat * p.sg;
+  float* Mb = p.M ? p.M + (int64_t)mat * p.sm : nullptr;
+  T* Sb = reinterpret_cast<T*>(p.out_same) + (int64_t)mat * p.s_same;
+  double ss = 0.0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t v = (int64_t)blockIdx.x * PREP_SV + h * 256 + tid;
+    if (v >= nvec) continue;
+    const int64_t r = v / vpr;
+    const int c = (int)(v - r * vpr) * 8;
+    float x[8];
+    ld8<T>(Gb + r * p.ldg + c, x);
+    if (Mb) {
+      const int64_t mi = r * p.ldm + c;
+      float m[8];
+      ld8<float>(Mb + mi, m);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        m[e] = p.mu * m[e] + (1.f - p.mu) * x[e];
+        x[e] = p.nesterov ? p.mu * m[e] + (1.f - p.mu) * x[e] : m[e];
+      }
+      st8<float>(Mb + mi, m);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = round_to<T>(x[e]);
+      ss += (double)x[e] * (double)x[e];
+    }
+    st8<T>(Sb + r * p.ld_same + c, x);
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) p.partials[(int64_t)mat * p.tiles + blockIdx.x] = red[0];
+}
+
 __global__ void __launch_bounds__(256) finalize_kernel(const double* partials, int tiles,
                                                        float eps, float* svec,
                                                        int32_t* flags) {

@@ -571,7 +571,6 @@ int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, 
     a.M = reinterpret_cast<float*>(src.M->ptr) + b0 * src.M->stride;
     a.ldm = src.M->ld; a.sm = src.M->stride; a.mu = src.mu; a.nesterov = src.nesterov;
   }
-  dim3 grid(g.prep_tiles, (unsigned)nb);
   // vectorised path: every row and the momentum buffer 16-byte aligned, widths multiples of 8
   auto al = [](const void* ptr, int64_t ld, int64_t stride, int64_t batch) {
     return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && ld % 8 == 0 && (batch == 1 || stride % 8 == 0);
@@ -579,8 +578,18 @@ int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, 
   const bool vec = G->dtype == c.io_dt && G->cols % 8 == 0 && G->rows % 8 == 0 &&
                    al(G->ptr, G->ld, G->stride, G->batch) &&
                    (!src.M || al(src.M->ptr, src.M->ld, src.M->stride, src.M->batch));
+  // without a transpose the aligned case streams whole rows; its partials (one per 4096
+  // elements) never outnumber the 64 x 64 tiles the partial buffer is sized for
+  const bool stream = vec && !g.trans;
+  const int64_t sblocks = ((int64_t)G->rows * G->cols / 8 + PREP_SV - 1) / PREP_SV;
+  const int tiles = stream ? (int)sblocks : g.prep_tiles;
+  a.tiles = tiles;
+  dim3 grid((unsigned)tiles, (unsigned)nb);
   int st = launch(K_PREP, s, [&] {
     if (!vec) hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, s, a);
+    else if (stream && c.io_dt == BF16) hipLaunchKernelGGL(prep_stream_kernel<__bf16>, grid, dim3(256), 0, s, a);
+    else if (stream && c.io_dt == F16) hipLaunchKernelGGL(prep_stream_kernel<_Float16>, grid, dim3(256), 0, s, a);
+    else if (stream) hipLaunchKernelGGL(prep_stream_kernel<float>, grid, dim3(256), 0, s, a);
     else if (c.io_dt == BF16) hipLaunchKernelGGL(prep_vec_kernel<__bf16>, grid, dim3(256), 0, s, a);
     else if (c.io_dt == F16) hipLaunchKernelGGL(prep_vec_kernel<_Float16>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(prep_vec_kernel<float>, grid, dim3(256), 0, s, a);
@@ -589,7 +598,6 @@ int run_prep(const Source& src, const Geo& g, const NsConf& c, const Layout& L, 
   double* part = at<double>(ws, L.partials);
   float* sv = at<float>(ws, L.svec);
   int32_t* fl = flags ? flags + b0 : nullptr;
-  const int tiles = g.prep_tiles;
   const float eps = c.eps;
   return launch(K_FINALIZE, s, [&] {
     hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)nb), dim3(256), 0, s, part, tiles, eps, sv, fl);
