@@ -39,8 +39,8 @@ def kind_work(kind: str, groups):
            "gemm_square": (lambda n, m: 2 * n ** 3, "flop", "mfma"),
            "gemm_syrk": (lambda n, m: flops.sym_flops(n, m), "flop", "mfma"),
            "gemm_rect": (lambda n, m: flops.rect_flops(n, m), "flop", "mfma"),
-           # read G (bf16) and M (fp32), write M (fp32) and the two bf16 copies of N
-           "prep_norm": (lambda n, m: n * m * (2 + 4 + 4 + 2 + 2), "byte", "hbm")}
+           # read G (bf16) and M (fp32), write M (fp32) and the bf16 copy of N
+           "prep_norm": (lambda n, m: n * m * (2 + 4 + 4 + 2), "byte", "hbm")}
     if kind not in per:
         return None
     f, unit, bound = per[kind]
@@ -215,6 +215,46 @@ def cpu_baseline(G_host, W_host, budget_s: float, variant: str):
                       f"numpy fp64, {dt:.1f} s"}
 
 
+def vendor_gemm(args):
+    """Context for the roofline: the vendor library's plain batched products (torch.bmm, fp16,
+    contiguous operands, no epilogue) on the shapes of the step's products. Not part of the
+    library; prints one JSON line of its own."""
+    import torch
+    B, n, m = args.batch, min(args.rows, args.cols), max(args.rows, args.cols)
+    dt = torch.float16
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    A = torch.randn(B, n, n, device="cuda", dtype=dt, generator=gen)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    C = torch.randn(B, n, n, device="cuda", dtype=dt, generator=gen)
+    D = torch.empty(B, n, n, device="cuda", dtype=dt)
+    ms = timed(lambda: torch.bmm(A, C, out=D))
+    out["square_nxnxn"] = {"ms": ms, "tflops": 2 * B * n ** 3 / ms / 1e9}
+    del C, D
+    X = torch.randn(B, n, m, device="cuda", dtype=dt, generator=gen)
+    Y = torch.empty(B, n, m, device="cuda", dtype=dt)
+    ms = timed(lambda: torch.bmm(A, X, out=Y))
+    out["rect_nxnxm"] = {"ms": ms, "tflops": 2 * B * n * n * m / ms / 1e9}
+    del Y
+    Xt = X.transpose(1, 2).contiguous()
+    R = torch.empty(B, n, n, device="cuda", dtype=dt)
+    ms = timed(lambda: torch.bmm(X, Xt, out=R))
+    out["gram_nxmxn_full"] = {"ms": ms, "tflops": 2 * B * n * n * m / ms / 1e9}
+    print(json.dumps({"comparison": "torch.bmm fp16 (vendor GEMM), plain batched products",
+                      "batch": B, "n": n, "m": m, "products": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +275,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="comparison only: time torch.bmm (the vendor GEMM library) on the plain "
+                         "products of the step's shapes and print that instead of the bench line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -253,6 +296,8 @@ def main():
         copy_probe(args.copy_probe_mib)
     if args.workload == "adamw":
         return bench_adamw(args)
+    if args.vendor_gemm:
+        return vendor_gemm(args)
     if args.workload == "experts":
         shapes = [(args.batch, args.rows, args.cols)]
         workload = f"kimi_k2_experts_{args.batch}x{args.rows}x{args.cols}_bf16_gaussian_plus_rank32_spike"
