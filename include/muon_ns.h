@@ -30,6 +30,9 @@
  *    norm is zero (the output is then exactly zero), bit2 = a non-finite output value.
  *  - Calls that share a workspace must be ordered on one stream; calls on different
  *    streams need different workspaces.
+ *  - Size limit: one n x m iterate (m rounded up to a multiple of 8, in the wider of the
+ *    input and iterate dtypes) must span at most 2^31 bytes, e.g. 32768 x 32768 in bf16;
+ *    larger matrices return MNS_ERR_SHAPE.
  */
 #ifndef MUON_NS_H
 #define MUON_NS_H

@@ -127,7 +127,7 @@ struct NsConf {
   uint32_t restart;
 };
 
-int check_params(const mns_ns_params* p, int io_dt, NsConf* c) {
+int check_params(const mns_ns_params* p, int io_dt, NsConf* c, const mns_tensor* G, int ngroups) {
   if (!p) return MNS_ERR_ARG;
   if (p->steps < 1 || p->steps > 64) return MNS_ERR_ARG;
   if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return MNS_ERR_ARG;
@@ -147,6 +147,13 @@ int check_params(const mns_ns_params* p, int io_dt, NsConf* c) {
   c->io_dt = io_dt;
   c->it_dt = p->iter_dtype;
   c->restart = p->restart_mask;
+  // the products address each operand matrix with 32-bit byte offsets (offsets from 2^31 up
+  // are their zero-fill sentinel): one n x m iterate must span at most 2^31 bytes
+  const int64_t es = std::max(dtype_size(io_dt), dtype_size(p->iter_dtype));
+  for (int i = 0; i < ngroups; ++i) {
+    const int64_t n = std::min(G[i].rows, G[i].cols), m = std::max(G[i].rows, G[i].cols);
+    if (n * round_up(m, 8) * es > (int64_t(1) << 31)) return MNS_ERR_SHAPE;
+  }
   return MNS_OK;
 }
 
@@ -860,7 +867,7 @@ int ns_entry(int variant, const mns_tensor* G, const mns_tensor* O, const mns_ns
   if (O->dtype != G->dtype) return MNS_ERR_DTYPE;
   if (overlap(G, O)) return MNS_ERR_ARG;
   NsConf c;
-  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (int st = check_params(p, G->dtype, &c, G, 1)) return st;
   if (!ws) return MNS_ERR_WORKSPACE;
   Source src;
   src.G = G;
@@ -970,7 +977,7 @@ int mns_workspace_bytes(int variant, const mns_tensor* G, const mns_ns_params* p
   if (variant != MNS_VARIANT_STANDARD && variant != MNS_VARIANT_GRAM) return MNS_ERR_ARG;
   if (int st = check_tensor(G, false)) return st;
   NsConf c;
-  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (int st = check_params(p, G->dtype, &c, G, 1)) return st;
   const int64_t chunk = max_batch_chunk <= 0 ? G->batch : std::min(max_batch_chunk, G->batch);
   *bytes = plan(variant, geometry(G), c, chunk).total;
   return MNS_OK;
@@ -992,7 +999,7 @@ int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, con
   if (int st = check_step(W, G, M, U_out)) return st;
   if (int st = check_step_params(sp)) return st;
   NsConf c;
-  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (int st = check_params(p, G->dtype, &c, G, 1)) return st;
   if (!ws) return MNS_ERR_WORKSPACE;
   Source src;
   FinalOut fo;
@@ -1010,7 +1017,7 @@ int mns_workspace_bytes_grouped(int variant, int ngroups, const mns_tensor* G, c
     if (G[i].dtype != G[0].dtype) return MNS_ERR_DTYPE;
   }
   NsConf c;
-  if (int st = check_params(p, G[0].dtype, &c)) return st;
+  if (int st = check_params(p, G[0].dtype, &c, G, ngroups)) return st;
   *bytes = grouped_bytes(variant, ngroups, G, c);
   return MNS_OK;
 }
@@ -1032,7 +1039,7 @@ int muon_step_grouped(int ngroups, const mns_tensor* W, const mns_tensor* G, con
   }
   if (any_overlap(all, na)) return MNS_ERR_ARG;
   NsConf c;
-  if (int st = check_params(p, G[0].dtype, &c)) return st;
+  if (int st = check_params(p, G[0].dtype, &c, G, ngroups)) return st;
   if (!ws) return MNS_ERR_WORKSPACE;
   Source srcs[MNS_MAXG];
   FinalOut fos[MNS_MAXG];
@@ -1057,7 +1064,7 @@ static int ns_grouped(int variant, int ngroups, const mns_tensor* G, const mns_t
     for (int j = 0; j < ngroups; ++j)
       if (overlap(&G[i], &O[j])) return MNS_ERR_ARG;
   NsConf c;
-  if (int st = check_params(p, G[0].dtype, &c)) return st;
+  if (int st = check_params(p, G[0].dtype, &c, G, ngroups)) return st;
   if (!ws) return MNS_ERR_WORKSPACE;
   Source srcs[MNS_MAXG];
   FinalOut fos[MNS_MAXG];
@@ -1087,7 +1094,7 @@ int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params*
   if (overlap(G, O)) return MNS_ERR_ARG;
   if (!trace) return MNS_ERR_ARG;
   NsConf c;
-  if (int st = check_params(p, G->dtype, &c)) return st;
+  if (int st = check_params(p, G->dtype, &c, G, 1)) return st;
   if (c.steps < 2) return MNS_ERR_ARG;
   if (!ws) return MNS_ERR_WORKSPACE;
   mns_tensor g1 = *G, o1 = *O;

@@ -67,6 +67,27 @@ def test_workspace_query_is_host_only_and_monotone(L):
     assert bt.value == out[ops.GRAM]
 
 
+def test_matrices_beyond_the_32_bit_operand_range_are_rejected_up_front(L):
+    """One n x m iterate may span at most 2^31 bytes (the products' 32-bit operand offsets):
+    the limit is reported by the workspace query and by the call itself, before any HIP call
+    (the pointers here are not device memory)."""
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    b = ctypes.c_size_t()
+    ok = _t(ops, batch=1, rows=32768, cols=32768)                  # exactly 2^31 bytes
+    big = _t(ops, batch=1, rows=32768, cols=32776)                 # 2^31 + 512 KiB
+    tall = _t(ops, batch=1, rows=32776, cols=32768)                # same, transposed orientation
+    assert L.mns_workspace_bytes(ops.GRAM, ctypes.byref(ok), ctypes.byref(p), 0, ctypes.byref(b)) == 0
+    for t in (big, tall):
+        assert L.mns_workspace_bytes(ops.GRAM, ctypes.byref(t), ctypes.byref(p), 0, ctypes.byref(b)) == -3
+        o = _t(ops, ptr=0x7e0000000000, batch=1, rows=t.rows, cols=t.cols)
+        assert L.gram_ns_batched(ctypes.byref(t), ctypes.byref(o), ctypes.byref(p),
+                                 ctypes.c_void_p(0x7f0000000000), 1 << 40, None, None) == -3
+    # a grouped query with one oversized group fails as a whole
+    G = (ops.MnsTensor * 2)(_t(ops, batch=1, rows=64, cols=64), big)
+    assert L.mns_workspace_bytes_grouped(ops.GRAM, 2, G, ctypes.byref(p), ctypes.byref(b)) == -3
+
+
 def test_argument_errors_return_before_any_hip_call(L):
     from newton_schulz_matrix_muon_amd import ops
     p = ops.ns_params(io_dtype=ops.BF16)
