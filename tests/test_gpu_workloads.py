@@ -142,3 +142,28 @@ def test_k2_dense_3x7168x18432_structured(torch, ops):
             e = rel_fro(got, ref)
             say(f"  {variant} matrix {b}: sampled-entry rel_F {e:.3e}")
             assert e <= TOL
+
+
+@pytest.mark.parametrize("variant", ["standard", "gram_stabilized"])
+@pytest.mark.parametrize("shape", [(24, 1000, 1500), (24, 1500, 1000)])
+def test_ragged_batch_on_the_large_tile_path(torch, ops, variant, shape):
+    """n = 1000 (a k tail inside a 64-wide k-stage) and m = 1500 (not a multiple of 8 or of the
+    256-wide tile), large enough that the rectangular products take the 256 x 256 DMA kernel
+    with X read k-major; both orientations. Sampled matrices against the oracle."""
+    say(f"case ragged large-tile {shape} {variant}")
+    B, r, c = shape
+    n, m = min(r, c), max(r, c)
+    assert B * math.ceil(n / 256) * math.ceil(m / 256) >= 512      # the 256-tile policy applies
+    code = ops.GRAM if variant == "gram_stabilized" else ops.STANDARD
+    ns = (lambda x: oracle.ns_gram(x, restarts=(2,))) if code == ops.GRAM else oracle.ns_standard
+    G = synth.torch_lowrank_plus_noise(B, r, c, power=0.7, noise=0.05, workload_index=1,
+                                       seed_offset=4242, device="cuda")
+    O = ops.gram_ns(G) if code == ops.GRAM else ops.muon_ns(G)
+    torch.cuda.synchronize()
+    assert O.shape == G.shape
+    for b in (0, B - 1):
+        ref = ns(to_np(G[b]))
+        e = rel_fro(to_np(O[b]), ref)
+        ok, info = band_ok(to_np(O[b]), ref, TOL)
+        say(f"  matrix {b}: rel_F {e:.3e}, band {info}")
+        assert e <= TOL and ok
