@@ -267,10 +267,14 @@ def test_muon_step_transposed_orientation(torch, ops):
 
 
 @pytest.mark.parametrize("shape,wdt", [((6, 256, 512), "bf16"), ((4, 512, 256), "bf16"), ((3, 264, 520), "f16"),
-                                       ((2, 256, 768), "f32")])
+                                       ((2, 256, 768), "f32"),
+                                       # large enough for the 256 x 256 tiles: W row pass and,
+                                       # for the tall batch, the transposed column pass
+                                       ((24, 1000, 1512), "bf16"), ((24, 1512, 1000), "bf16")])
 def test_muon_step_weight_update_without_u_out(torch, ops, shape, wdt):
     """Without U_out the last product updates W in its own epilogue; it must agree with the
-    path that also writes U (to one unit in the last place of W) and flag non-finite outputs."""
+    path that also writes U (to one unit in the last place of W) and flag non-finite outputs.
+    U of the first matrix is checked against the oracle's Muon step."""
     say(f"case muon_step W update without U_out {shape} {wdt}")
     B, r, c = shape
     dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wdt]
@@ -294,6 +298,9 @@ def test_muon_step_weight_update_without_u_out(torch, ops, shape, wdt):
     e = np.floor(np.log2(np.maximum(np.maximum(np.abs(a), np.abs(b)), 2.0 ** -14)))
     tol = 2.0 ** (e - mant) + 4 * 2.0 ** -24 * ((1 - 0.02 * 0.1) * np.abs(w0) + 0.02 * np.abs(u))
     assert np.all(np.abs(a - b) <= tol), float(np.max(np.abs(a - b) / tol))
+    _, _, Un = oracle.muon_step(np.zeros((r, c)), to_np(G[0]), np.zeros((r, c)), 0.02, 0.95, 0.1,
+                                nesterov=True, scale_coeff=0.2, ns=lambda x: oracle.ns_gram(x, restarts=(2,)))
+    assert rel_fro(u[0], Un) < 2e-2
     # a NaN in one gradient: that matrix's flags report the non-finite output
     G[1, 3, 5] = float("nan")
     flags = torch.zeros(B, dtype=torch.int32, device="cuda")
