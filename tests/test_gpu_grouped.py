@@ -131,3 +131,24 @@ def test_grouped_k2_structure_reduced(torch, ops):
     O = to_np(outs[2][0])
     assert rel_fro(O, oracle.ns_gram(to_np(Gs[2][0]), restarts=(2,))) < TOL
     assert math.isfinite(float(outs[0].float().abs().max()))
+
+
+def test_grouped_k2_full_size_equals_single_calls(torch, ops):
+    """The whole Kimi-K2 Muon step's matrices at full size in one grouped call (432 x 2048 x
+    7168 up/gate, 216 x 7168 x 2048 down, 3 x 7168 x 18432 dense): the 256 x 256 kernels with
+    every group's tiles split over the XCDs, bit for bit equal to one call per group; the first
+    matrix of the two expert groups against the oracle."""
+    say("case grouped K2 full size")
+    shapes = [(432, 2048, 7168), (216, 7168, 2048), (3, 7168, 18432)]
+    Gs = [synth.torch_gaussian_plus_spike(b, r, c, workload_index=2, device="cuda") for b, r, c in shapes]
+    outs = ops.gram_ns_grouped(Gs)
+    torch.cuda.synchronize()
+    for G, O in zip(Gs, outs):
+        S = ops.gram_ns(G)
+        torch.cuda.synchronize()
+        assert torch.equal(O, S)
+        del S
+    for i in (0, 1):
+        e = rel_fro(to_np(outs[i][0]), oracle.ns_gram(to_np(Gs[i][0]), restarts=(2,)))
+        say(f"  group {i} matrix 0: rel_F {e:.3e}")
+        assert e < TOL
