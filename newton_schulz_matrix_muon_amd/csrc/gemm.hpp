@@ -13,11 +13,12 @@
 // writes each value to (i, j) and (j, i), so stored symmetric matrices are exactly
 // symmetric.
 //
-// Tile: 128 x 128 per workgroup of 4 waves (2 x 2), each wave 64 x 64 as 2 x 2 blocks of
-// the 32x32 MFMA (bf16/f16: v_mfma_f32_32x32x16, fp32: v_mfma_f32_32x32x2f32), fp32
-// accumulation. K is staged through LDS 128 bytes per row at a time (64 half-precision or
-// 32 fp32 values), double-buffered, rows padded to 144 bytes so the 16-byte fragment reads
-// of 16 consecutive rows hit distinct banks.
+// Tiles (TileCfg): every wave computes 64 x 64 as 2 x 2 blocks of the 32x32 MFMA (bf16/f16:
+// v_mfma_f32_32x32x16, fp32: v_mfma_f32_32x32x2f32) with fp32 accumulation, and K moves
+// through LDS 128 bytes per operand row at a time (64 half-precision or 32 fp32 values).
+// Large problems: 256 x 256 per workgroup of 16 waves, operands DMA'd global -> LDS into a
+// 2-deep ring of XOR-swizzled k-stages. Small problems: 128 x 128 per workgroup of 4 waves,
+// staged through registers into LDS rows padded to 144 bytes.
 //
 // Epilogue (per matrix b, scale s_b from the norm kernel):
 //   v = s_b^spow * (c2 * acc + c1 * E[i][j]) + c0 * [i == j < M]
