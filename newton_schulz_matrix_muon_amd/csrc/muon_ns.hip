@@ -650,27 +650,35 @@ int run_standard(const Part* P, int np, const NsConf& c, hipStream_t s) {
   for (int k = 1; k <= c.steps; ++k) {
     const float a_k = c.coeff[k - 1][0], b_k = c.coeff[k - 1][1], c_k = c.coeff[k - 1][2];
     const bool first = k == 1;
+    // With fp16 or fp32 operands the a X term rides in the product, X <- (a I + b A + c A^2) X
+    // (the guide's own form for the cubic, B = 1.5 I - 0.5 A), which spares the product's
+    // epilogue a read of X. The first step multiplies the caller's X in its input dtype, and a
+    // bf16 B would round the diagonal a + ... to 8 bits, so there a X stays an fp32 epilogue
+    // term; likewise for bf16 iterates.
+    const bool fold = !first && xdt != BF16;
     // A = X X^T (scaled by s^2 on the unnormalised first iterate)
     if (int st = run_all(P, np, K_SYRK, s, [&](int i) {
           return gram_prod(B[i].X[cur], xdt, P[i].g, B[i].A, it, B[i].sv, first ? 2 : 0);
         })) return st;
-    // B = b A + c A^2, stored in the dtype of X (the two are the operands of B X)
+    // B = [a I +] b A + c A^2, stored in the dtype of X (the two are the operands of B X)
     if (int st = run_all(P, np, K_SYMPROD, s, [&](int i) {
           const Geo& g = P[i].g;
           Prod q = sym_prod(B[i].A, B[i].A, it, g, B[i].Bm, xdt);
-          q.c0 = 0.f; q.c1 = b_k; q.c2 = c_k;
+          q.c0 = fold ? a_k : 0.f; q.c1 = b_k; q.c2 = c_k;
           q.E = B[i].A; q.e_dt = it; q.lde = g.ldn; q.sE = (int64_t)g.n * g.ldn; q.e_rows = g.n;
           q.e_cols = (int)g.ldn;
           return q;
         })) return st;
-    // X <- s (a X + B X)
+    // X <- s (a X + B X), or B X with the folded B
     if (int st = run_all(P, np, K_RECT, s, [&](int i) {
           const Geo& g = P[i].g;
           Prod q = rect_prod(B[i].Bm, B[i].X[cur], xdt, g);
           q.svec = B[i].sv; q.spow = first ? 1 : 0;
-          q.c1 = a_k; q.c2 = 1.f;
-          q.E = B[i].X[cur]; q.e_dt = xdt; q.lde = g.ldm; q.sE = (int64_t)g.n * g.ldm; q.e_rows = g.n;
-          q.e_cols = (int)g.ldm;
+          if (!fold) {
+            q.c1 = a_k; q.c2 = 1.f;
+            q.E = B[i].X[cur]; q.e_dt = xdt; q.lde = g.ldm; q.sE = (int64_t)g.n * g.ldm; q.e_rows = g.n;
+            q.e_cols = (int)g.ldm;
+          }
           if (k < c.steps) set_internal_x_out(q, B[i].X[cur ^ 1], it, g);
           else set_final(q, P[i].fo, g, P[i].b0);
           return q;
