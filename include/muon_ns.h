@@ -40,6 +40,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Exported entry points (the library is built with hidden default visibility). */
+#ifndef MNS_API
+#define MNS_API __attribute__((visibility("default")))
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -116,7 +121,7 @@ typedef struct mns_step_params {
  * then process the batch in the largest chunks that fit. Host-only; no HIP call.
  * Returns MNS_OK and *bytes, or an argument error.
  */
-int mns_workspace_bytes(int variant, const mns_tensor* G, const mns_ns_params* p,
+MNS_API int mns_workspace_bytes(int variant, const mns_tensor* G, const mns_ns_params* p,
                         int64_t max_batch_chunk, size_t* bytes);
 
 /*
@@ -125,7 +130,7 @@ int mns_workspace_bytes(int variant, const mns_tensor* G, const mns_ns_params* p
  * G: input batch (F32, BF16 or F16). O: output, same batch/rows/cols/dtype as G, must not
  * overlap G. ws/ws_bytes: device workspace. flags: device int32 [batch] or NULL.
  */
-int muon_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+MNS_API int muon_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
                     void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
 /*
@@ -135,7 +140,7 @@ int muon_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_param
  * R <- Z R Z (when k < K); the output is Q X. Equal to muon_ns_batched in exact arithmetic.
  * Arguments as for muon_ns_batched.
  */
-int gram_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+MNS_API int gram_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
                     void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
 /*
@@ -148,7 +153,7 @@ int gram_ns_batched(const mns_tensor* G, const mns_tensor* O, const mns_ns_param
  * U_out: NULL, or a buffer of G's shape (F32/BF16/F16) that receives U (before lr).
  * N is stored in G's dtype before Newton-Schulz. Arguments otherwise as above.
  */
-int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
+MNS_API int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
               const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
               void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
@@ -168,13 +173,13 @@ int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
  *  Errors as for the single-group calls, plus MNS_ERR_ARG for ngroups outside 1 .. 4 or any
  *  two output buffers (or an output and an input) that overlap.
  */
-int mns_workspace_bytes_grouped(int variant, int ngroups, const mns_tensor* G,
+MNS_API int mns_workspace_bytes_grouped(int variant, int ngroups, const mns_tensor* G,
                                 const mns_ns_params* p, size_t* bytes);
-int muon_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+MNS_API int muon_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
                     void* ws, size_t ws_bytes, int32_t* flags, void* stream);
-int gram_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
+MNS_API int gram_ns_grouped(int ngroups, const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p,
                     void* ws, size_t ws_bytes, int32_t* flags, void* stream);
-int muon_step_grouped(int ngroups, const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
+MNS_API int muon_step_grouped(int ngroups, const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
                       const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
                       void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
@@ -201,7 +206,7 @@ typedef struct mns_adamw_params {
  * Errors: MNS_ERR_ARG (null pointer, numel < 0, non-finite or out-of-range hyper-parameter,
  * beta outside [0, 1), overlap), MNS_ERR_DTYPE, MNS_ERR_HIP.
  */
-int adamw_step(int ntensors, void* const* params, const void* const* grads, float* const* exp_avg,
+MNS_API int adamw_step(int ntensors, void* const* params, const void* const* grads, float* const* exp_avg,
                float* const* exp_avg_sq, const int64_t* numels, int32_t dtype,
                const mns_adamw_params* ap, void* stream);
 
@@ -213,17 +218,17 @@ int adamw_step(int ntensors, void* const* params, const void* const* grads, floa
  * trace: device float [K-1][n][n] row-major, n = min(rows, cols). O: as in gram_ns_batched
  * (only matrix 0 is written). ws: workspace for a batch of one. Requires K >= 2.
  */
-int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,
+MNS_API int gram_ns_trace(const mns_tensor* G, const mns_tensor* O, const mns_ns_params* p, void* ws,
                    size_t ws_bytes, float* trace, void* stream);
 
 /* Static English text for a status code (never NULL). */
-const char* mns_status_string(int code);
+MNS_API const char* mns_status_string(int code);
 
 /* The hipError_t of the last HIP failure on the calling thread (0 if none). */
-int mns_last_hip_error(void);
+MNS_API int mns_last_hip_error(void);
 
 /* ABI version of this library (major * 10000 + minor * 100 + patch). */
-int mns_version(void);
+MNS_API int mns_version(void);
 
 /*
  * Per-kernel-kind launch timing with HIP events recorded on the call's stream around each
@@ -236,11 +241,11 @@ int mns_version(void);
  *  mns_kernel_kind_name(kind)      static name of a kind ("gemm_rect", ...), or NULL.
  * The query returns MNS_ERR_ARG for an unknown kind and MNS_ERR_HIP on an event failure.
  */
-int mns_timing_enable(int on);
-int mns_timing_reset(void);
-int mns_timing_query(int kind, double* total_ms, int64_t* launches);
-int mns_timing_kinds(void);
-const char* mns_kernel_kind_name(int kind);
+MNS_API int mns_timing_enable(int on);
+MNS_API int mns_timing_reset(void);
+MNS_API int mns_timing_query(int kind, double* total_ms, int64_t* launches);
+MNS_API int mns_timing_kinds(void);
+MNS_API const char* mns_kernel_kind_name(int kind);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "muon_ns.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+    names = re.findall(r"^\s*(?:MNS_API\s+)?(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                        text, flags=re.M)
     return sorted(set(names))
 
@@ -32,8 +32,24 @@ def test_header_declares_the_entry_points():
 
 
 def test_library_exports_every_declared_symbol(L):
-    for name in declared_functions():
+    names = declared_functions()
+    assert len(names) >= 18
+    for name in names:
         assert hasattr(L, name), name
+
+
+def test_library_exports_nothing_else():
+    """Built with hidden visibility: the dynamic symbol table holds the header's functions and
+    no internal host function or kernel launch stub."""
+    import shutil
+    import subprocess
+    from newton_schulz_matrix_muon_amd import ops
+    if not shutil.which("nm"):
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {l.split()[-1] for l in out.splitlines() if len(l.split()) == 3 and l.split()[1] == "T"}
+    assert funcs == set(declared_functions())
 
 
 def test_status_strings_and_version(L):
