@@ -209,7 +209,11 @@ def cpu_baseline(G_host, W_host, budget_s: float, variant: str):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    from newton_schulz_matrix_muon_amd import flops
+    r, c = G_host[0].shape
+    per = flops.gram_flops(r, c) if variant == "gram" else flops.standard_flops(r, c)
     return {"value": done / dt, "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
+            "fp64_gflops": done * per / dt / 1e9,
             "sample": f"{done} of the batch's matrices, fused Muon step with "
                       f"{'stabilized Gram' if variant == 'gram' else 'standard'} Newton-Schulz, "
                       f"numpy fp64, {dt:.1f} s"}
@@ -258,8 +262,8 @@ def vendor_gemm(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--variant", choices=["gram", "standard"], default="gram")
     ap.add_argument("--workload", choices=["experts", "k2_full", "k2_hybrid", "adamw"], default="experts",
                     help="experts: one batch of --batch x --rows x --cols expert matrices (default "
