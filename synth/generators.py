@@ -61,14 +61,18 @@ def orthonormal(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
 
 
 def lowrank_plus_noise(rng: np.random.Generator, rows: int, cols: int, power: float,
-                       noise: float, normalize: bool = True) -> np.ndarray:
+                       noise: float, normalize: bool = True, relative: bool = False) -> np.ndarray:
     """G = U diag(i^-power) V^T + noise * E (E ~ N(0,1) per entry), optionally scaled to
-    unit Frobenius norm. fp64, host side."""
+    unit Frobenius norm. relative: scale the noise term instead so that its Frobenius norm is
+    noise times the signal's (keeps the power law above the noise). fp64, host side."""
     r = min(rows, cols)
     U = orthonormal(rng, rows, r)
     V = orthonormal(rng, cols, r)
     s = np.arange(1, r + 1, dtype=np.float64) ** (-power)
-    G = (U * s) @ V.T + noise * rng.standard_normal((rows, cols))
+    E = rng.standard_normal((rows, cols))
+    if relative:
+        E *= np.linalg.norm(s) / np.linalg.norm(E)
+    G = (U * s) @ V.T + noise * E
     if normalize:
         G = G / np.linalg.norm(G)
     return G
@@ -153,8 +157,10 @@ def _t_orthonormal(gen, batch, rows, cols, device):
 
 def torch_lowrank_plus_noise(batch: int, rows: int, cols: int, power: float, noise: float,
                              workload_index: int, seed_offset: int = 0, device="cuda",
-                             dtype=None, normalize: bool = True, chunk: int = 8):
-    """Device-side batch of low-rank-plus-noise matrices (fp32 arithmetic, stored in ``dtype``)."""
+                             dtype=None, normalize: bool = True, chunk: int = 8,
+                             relative: bool = False):
+    """Device-side batch of low-rank-plus-noise matrices (fp32 arithmetic, stored in ``dtype``);
+    ``relative`` as in lowrank_plus_noise."""
     torch = _torch()
     dtype = torch.bfloat16 if dtype is None else dtype
     out = torch.empty(batch, rows, cols, device=device, dtype=dtype)
@@ -166,7 +172,10 @@ def torch_lowrank_plus_noise(batch: int, rows: int, cols: int, power: float, noi
         U = _t_orthonormal(gen, nb, rows, r, device)
         V = _t_orthonormal(gen, nb, cols, r, device)
         G = torch.matmul(U * s, V.transpose(-1, -2).contiguous())
-        G += noise * torch.randn(nb, rows, cols, generator=gen, device=device, dtype=torch.float32)
+        E = torch.randn(nb, rows, cols, generator=gen, device=device, dtype=torch.float32)
+        if relative:
+            E *= torch.linalg.vector_norm(s) / torch.linalg.vector_norm(E, dim=(-2, -1), keepdim=True)
+        G += noise * E
         if normalize:
             G /= torch.linalg.vector_norm(G, dim=(-2, -1), keepdim=True)
         out[b0:b0 + nb] = G.to(dtype)

@@ -167,3 +167,25 @@ def test_ragged_batch_on_the_large_tile_path(torch, ops, variant, shape):
         ok, info = band_ok(to_np(O[b]), ref, TOL)
         say(f"  matrix {b}: rel_F {e:.3e}, band {info}")
         assert e <= TOL and ok
+
+
+@pytest.mark.parametrize("variant", ["standard", "gram_stabilized"])
+def test_expert_batch_relative_noise(torch, ops, variant):
+    """The second reading of the expert batch's noise: 0.05 of the signal's Frobenius norm
+    instead of 0.05 N(0, 1) per entry, which keeps the i^-0.7 spectrum above the noise (the
+    harder case: singular values spread over three decades). 64 x 1408 x 2048 bf16, NS alone;
+    sampled matrices against the oracle."""
+    say(f"case expert 64x1408x2048 relative noise {variant}")
+    B, r, c = 64, 1408, 2048
+    code = ops.GRAM if variant == "gram_stabilized" else ops.STANDARD
+    ns = (lambda x: oracle.ns_gram(x, restarts=(2,))) if code == ops.GRAM else oracle.ns_standard
+    G = synth.torch_lowrank_plus_noise(B, r, c, power=0.7, noise=0.05, workload_index=1,
+                                       seed_offset=5000, device="cuda", relative=True)
+    O = ops.gram_ns(G) if code == ops.GRAM else ops.muon_ns(G)
+    torch.cuda.synchronize()
+    for b in (0, 41):
+        ref = ns(to_np(G[b]))
+        e = rel_fro(to_np(O[b]), ref)
+        ok, info = band_ok(to_np(O[b]), ref, TOL)
+        say(f"  matrix {b}: rel_F {e:.3e}, band {info}")
+        assert e <= TOL and ok
