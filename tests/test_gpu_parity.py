@@ -4,7 +4,6 @@ Bars: relative Frobenius error <= 1e-4 on the fp32 path and <= 2e-2 on the bf16/
 against the oracle's same variant, steps, coefficients and restart set, and every output
 singular value inside the oracle output's band widened by the same tolerance.
 """
-import math
 
 import numpy as np
 import pytest
