@@ -60,7 +60,7 @@ enum {
   MNS_ERR_SHAPE = -3,       /* rows/cols/batch < 1, ld < cols, stride too small, shape mismatch */
   MNS_ERR_WORKSPACE = -4,   /* workspace pointer NULL or smaller than one matrix needs */
   MNS_ERR_HIP = -5,         /* a HIP call failed; see mns_last_hip_error() */
-  MNS_ERR_UNSUPPORTED = -6  /* valid request this build does not implement */
+  MNS_ERR_UNSUPPORTED = -6  /* valid request the library does not implement */
 };
 
 /* A strided batch of row-major matrices (see conventions above). dtype is an mns_dtype. */
