@@ -4,10 +4,11 @@
 //    when the caller's matrix is m x n), zero-fills its padded columns, and emits a
 //    deterministic per-tile partial of sum x^2 (the Frobenius norm, guide's normalisation).
 //    With momentum enabled it first applies the Muon momentum rule to the fp32 buffer M and
-//    orthogonalizes N instead of G.
+//    orthogonalizes N instead of G. prep_vec_kernel is the same tile walk in 16-byte vectors
+//    for aligned buffers; prep_stream_kernel streams whole rows when no transpose is needed.
 //  - finalize_kernel: sums the partials of one matrix in a fixed order, s = 1/(sqrt + eps),
 //    and writes the per-matrix flags.
-//  - cast_kernel: dtype conversion of an n x ld internal matrix.
+//  - copy2d_kernel: strided copy with dtype conversion (the Gram-iterate trace).
 #pragma once
 
 #include "common.hpp"
@@ -288,16 +289,6 @@ __global__ void __launch_bounds__(256) finalize_kernel(const double* partials, i
     svec[mat] = (float)(1.0 / (nrm + (double)eps));
     if (flags) flags[mat] = (__builtin_isfinite(ss) ? 0 : 1) | (ss == 0.0 ? 2 : 0);
   }
-}
-
-__global__ void __launch_bounds__(256) cast_kernel(const void* src, int s_dt, void* dst, int d_dt,
-                                                   int64_t per_mat, int64_t s_stride,
-                                                   int64_t d_stride) {
-  const int mat = blockIdx.y;
-  const char* sb = reinterpret_cast<const char*>(src) + (int64_t)mat * s_stride * dtype_size(s_dt);
-  char* db = reinterpret_cast<char*>(dst) + (int64_t)mat * d_stride * dtype_size(d_dt);
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per_mat; i += (int64_t)gridDim.x * 256)
-    store_elem(db, d_dt, i, load_elem(sb, s_dt, i));
 }
 
 // rows x cols copy with dtype conversion between two strided 2-D buffers (diagnostics)

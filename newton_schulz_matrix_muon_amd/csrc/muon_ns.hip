@@ -2,7 +2,7 @@
 //
 // Validation happens before any HIP call. The planner lays out the caller's workspace,
 // splits the batch into chunks that fit, and enqueues, per chunk:
-//   prep (norm partials + the two internal copies of X) -> finalize (scale, flags)
+//   prep (norm partials + the one internal copy of X, in the n x m orientation) -> finalize (scale, flags)
 //   -> the product sequence of the chosen variant (gemm.hpp) with fused epilogues.
 // Everything is asynchronous on the caller's stream; nothing here synchronises.
 
