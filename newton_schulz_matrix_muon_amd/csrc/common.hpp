@@ -18,12 +18,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __host__ __device__ inline int dtype_size(int dt) { return dt == F32 ? 4 : 2; }
 
 // fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
-__device__ inline uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even, NaN kept quiet with its upper payload bits: gfx950's
+// v_cvt_pk_bf16_f32, which gives exactly the bits of the bitwise definition
+// ((u + 0x7fff + lsb) >> 16, NaN -> (u >> 16) | 0x40) for every one of the 2^32 inputs.
+__device__ inline uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -34,6 +32,15 @@ __device__ inline uint16_t f32_to_f16_bits(float f) {
 
 __device__ inline float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Two fp32 values -> two packed 16-bit values (lo in bits 0..15) with one packed conversion
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32; same rounding as the scalar conversions above).
+template <typename H>
+__device__ inline uint32_t pack2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef H h16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, h16x2));
 }
 
 // Load element `idx` of a buffer of runtime dtype `dt` as fp32.

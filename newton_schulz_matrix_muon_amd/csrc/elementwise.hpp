@@ -131,12 +131,7 @@ __device__ inline void st8(T* p, const float (&v)[8]) {
   } else {
     u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t lo, hi;
-      if constexpr (__is_same(T, __bf16)) { lo = f32_to_bf16_bits(v[2 * e]); hi = f32_to_bf16_bits(v[2 * e + 1]); }
-      else { lo = f32_to_f16_bits(v[2 * e]); hi = f32_to_f16_bits(v[2 * e + 1]); }
-      w[e] = lo | (hi << 16);
-    }
+    for (int e = 0; e < 4; ++e) w[e] = pack2<T>(v[2 * e], v[2 * e + 1]);
     *reinterpret_cast<u32x4*>(p) = w;
   }
 }

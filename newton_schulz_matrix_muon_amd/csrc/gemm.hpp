@@ -200,7 +200,7 @@ template <typename H> struct VecIO16 {
   static __device__ inline void store(void* p, int64_t idx, const float (&v)[8]) {
     u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = bits(v[2 * e]) | (bits(v[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) w[e] = pack2<H>(v[2 * e], v[2 * e + 1]);
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p) + idx) = w;
   }
 };
