@@ -23,6 +23,9 @@
  *    (no copy is asked of the caller).
  *  - Calls are asynchronous: they validate, enqueue kernels on `stream` (a hipStream_t;
  *    NULL = the null stream) and return. No host synchronisation happens inside a call.
+ *    A call enqueues kernel launches only (no memset, copy or event record unless timing
+ *    is switched on), so with a caller-supplied workspace it can be captured into a HIP
+ *    graph and replayed.
  *  - Argument errors are returned synchronously before any HIP call, and then nothing is
  *    enqueued. A failed launch returns MNS_ERR_HIP (detail: mns_last_hip_error()).
  *  - Numerical conditions are reported per matrix in `flags` (device int32 [batch], may be
