@@ -37,14 +37,23 @@ def bf16_steps(a, b):
     return np.abs(ordered(a) - ordered(b))
 
 
+def f16_steps(a, b):
+    """Number of fp16 representable steps between round_f16(a) and round_f16(b) (RNE)."""
+    def ordered(x):
+        bits = np.asarray(x, dtype=np.float16).view(np.int16).astype(np.int32)
+        mag = bits & 0x7FFF
+        return np.where(bits < 0, -mag, mag)
+    return np.abs(ordered(a) - ordered(b))
+
+
 def w_update_ok(Wg, W_prev, Ug, lr, wd, dtype="bf16"):
     """W after a step equals (1 - lr wd) W_prev - lr U, evaluated on the returned U and rounded
     once to the weight dtype: within one representable step of the exactly rounded value, or
     within the fp32 arithmetic error of the update (for results that nearly cancel)."""
     w_exp = (1.0 - lr * wd) * W_prev - lr * Ug
     slack = 4 * 2.0 ** -24 * (np.abs(W_prev) + lr * np.abs(Ug)) + 1e-30
-    if dtype == "bf16":
-        steps = bf16_steps(Wg, w_exp)
+    if dtype in ("bf16", "f16"):
+        steps = bf16_steps(Wg, w_exp) if dtype == "bf16" else f16_steps(Wg, w_exp)
         ok = (steps <= 1) | (np.abs(Wg - w_exp) <= slack)
     else:
         ok = np.abs(Wg - w_exp) <= slack + np.spacing(np.abs(w_exp).astype(np.float32)).astype(np.float64)

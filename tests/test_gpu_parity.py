@@ -248,6 +248,37 @@ def test_muon_step_two_steps(torch, ops, variant, wdt):
         W, M = Wg, Mg
 
 
+@pytest.mark.parametrize("variant,dt,nesterov", [("gram_stabilized", "f16", False),
+                                                 ("standard", "f32", True),
+                                                 ("gram_naive", "bf16", False)])
+def test_muon_step_dtypes_and_momentum_forms(torch, ops, variant, dt, nesterov):
+    """fp16 and fp32 gradients and weights, plain (non-Nesterov) momentum from a nonzero state,
+    and the naive Gram form, on a ragged shape: M, U and W against the oracle's Muon step."""
+    say(f"case muon_step {variant} {dt} nesterov={nesterov}")
+    B, r, c = 2, 200, 328
+    rng = synth.host_rng(99, 0)
+    G = np.stack([synth.lowrank_plus_noise(rng, r, c, 0.7, 0.05) for _ in range(B)])
+    Wd = torch.tensor(0.02 * rng.standard_normal((B, r, c)), dtype=tdtype(torch, dt), device="cuda")
+    Md = torch.tensor(0.1 * rng.standard_normal((B, r, c)), dtype=torch.float32, device="cuda")
+    Gd = torch.tensor(G, dtype=tdtype(torch, dt), device="cuda")
+    Ud = torch.empty(B, r, c, dtype=torch.float32, device="cuda")
+    W, M = to_np(Wd), to_np(Md)
+    lr, mu, wd = 0.02, 0.9, 0.05
+    code = ops.STANDARD if variant == "standard" else ops.GRAM
+    extra = {"restart_mask": 0} if variant == "gram_naive" else {}
+    ops.muon_step(Wd, Gd, Md, lr=lr, momentum=mu, weight_decay=wd, nesterov=nesterov,
+                  variant=code, U_out=Ud, **extra)
+    torch.cuda.synchronize()
+    Gh, Wg, Mg, Ug = to_np(Gd), to_np(Wd), to_np(Md), to_np(Ud)
+    for b in range(B):
+        Wn, Mn, Un = oracle.muon_step(W[b], Gh[b], M[b], lr, mu, wd, nesterov=nesterov,
+                                      scale_coeff=0.2, ns=oracle_fn(variant))
+        assert rel_fro(Mg[b], Mn) < 1e-6, b
+        assert rel_fro(Ug[b], Un) < TOL[dt], (b, rel_fro(Ug[b], Un))
+        ok, frac = w_update_ok(Wg[b], W[b], Ug[b], lr, wd, dt)
+        assert ok, (b, frac)
+
+
 def test_muon_step_transposed_orientation(torch, ops):
     say("case muon_step 300 x 120 (rows > cols)")
     rng = synth.host_rng(97, 0)
