@@ -279,6 +279,29 @@ def test_muon_step_dtypes_and_momentum_forms(torch, ops, variant, dt, nesterov):
         assert ok, (b, frac)
 
 
+def test_muon_step_with_zero_gradient_only_decays(torch, ops):
+    """G = 0 and M = 0: N has zero norm, the orthogonalized update is exactly zero (flag bit 1),
+    and W only decays: W <- (1 - lr wd) W, rounded once."""
+    say("case muon_step zero gradient")
+    B, r, c = 2, 96, 160
+    rng = synth.host_rng(100, 0)
+    W0 = 0.02 * rng.standard_normal((B, r, c))
+    for variant, code in (("standard", ops.STANDARD), ("gram_stabilized", ops.GRAM)):
+        Wd = torch.tensor(W0, dtype=torch.bfloat16, device="cuda")
+        W = to_np(Wd)
+        Gd = torch.zeros(B, r, c, dtype=torch.bfloat16, device="cuda")
+        Md = torch.zeros(B, r, c, dtype=torch.float32, device="cuda")
+        Ud = torch.full((B, r, c), float("nan"), dtype=torch.float32, device="cuda")
+        flags = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        ops.muon_step(Wd, Gd, Md, lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True,
+                      variant=code, U_out=Ud, flags=flags)
+        torch.cuda.synchronize()
+        assert flags.cpu().tolist() == [2, 2], (variant, flags.cpu().tolist())
+        assert torch.all(Ud == 0) and torch.all(Md == 0), variant
+        ok, frac = w_update_ok(to_np(Wd), W, np.zeros_like(W), 0.02, 0.1, "bf16")
+        assert ok, (variant, frac)
+
+
 def test_muon_step_transposed_orientation(torch, ops):
     say("case muon_step 300 x 120 (rows > cols)")
     rng = synth.host_rng(97, 0)
