@@ -144,6 +144,44 @@ def test_k2_dense_3x7168x18432_structured(torch, ops):
             assert e <= TOL
 
 
+def test_largest_accepted_matrix_32768x32768_structured(torch, ops):
+    """The largest matrix the library accepts: one n x m iterate of exactly 2^31 bytes
+    (32768 x 32768 bf16), where byte offsets reach the top of the 32-bit range and the
+    out-of-range sentinel equals the operand size. Known SVD (Kronecker factors), sampled
+    entries against the closed form, both variants."""
+    n = 32768
+    say(f"case largest matrix 1x{n}x{n} with known SVD")
+    spec = np.arange(1, n + 1, dtype=np.float64) ** -0.5
+    rng = np.random.default_rng([3, 9])
+    Ua = synth.orthonormal(rng, 128, 128); Ub = synth.orthonormal(rng, 256, 256)
+    Va = synth.orthonormal(rng, 128, 128); Vb = synth.orthonormal(rng, 256, 256)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    Ut = torch.kron(torch.tensor(Ua, **f32), torch.tensor(Ub, **f32))
+    Vt = torch.kron(torch.tensor(Va, **f32), torch.tensor(Vb, **f32))
+    st = torch.tensor(spec, **f32)
+    G = torch.matmul(Ut * st, Vt.t().contiguous()).to(torch.bfloat16).unsqueeze(0)
+    del Ut, Vt
+    nrm = float(sum(float((G[0, i:i + 2048].double() ** 2).sum()) for i in range(0, n, 2048)) ** 0.5)
+    torch.cuda.synchronize()
+    sel = np.random.default_rng(12)
+    rows = np.sort(sel.choice(n, 48, replace=False))
+    cols = np.sort(sel.choice(n, 48, replace=False))
+    Ur = np.stack([np.kron(Ua[i // 256], Ub[i % 256]) for i in rows])
+    Vr = np.stack([np.kron(Va[j // 256], Vb[j % 256]) for j in cols])
+    ref = oracle.ns_closed_form_entries(Ur, spec, Vr, fro_norm=nrm)
+    for variant in ("gram_stabilized", "standard"):
+        flags = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        O = ops.gram_ns(G, flags=flags) if variant != "standard" else ops.muon_ns(G, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0, (variant, int(flags.item()))
+        got = to_np(O[0][torch.tensor(rows, device="cuda")][:, torch.tensor(cols, device="cuda")])
+        e = rel_fro(got, ref)
+        say(f"  {variant}: sampled-entry rel_F {e:.3e}")
+        assert e <= TOL
+        del O
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("variant", ["standard", "gram_stabilized"])
 @pytest.mark.parametrize("shape", [(24, 1000, 1500), (24, 1500, 1000)])
 def test_ragged_batch_on_the_large_tile_path(torch, ops, variant, shape):
