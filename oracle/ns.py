@@ -163,6 +163,16 @@ def ns_closed_form_entries(U_rows, spectrum, V_rows, coeffs=None, eps: float = 1
     return (np.asarray(U_rows, dtype=np.float64) * f) @ np.asarray(V_rows, dtype=np.float64).T
 
 
+def momentum_update(M, G, momentum: float, nesterov: bool):
+    """Momentum accumulation of the guide's "Scalable Muon Optimizer" box, in its EMA form:
+    M_new = mu M + (1 - mu) G. The matrix handed to Newton-Schulz is M_new, or with Nesterov
+    the same rule applied once more to the updated buffer: N = mu M_new + (1 - mu) G.
+    Returns (M_new, N)."""
+    M_new = momentum * M + (1.0 - momentum) * G
+    N = momentum * M_new + (1.0 - momentum) * G if nesterov else M_new
+    return M_new, N
+
+
 def muon_step(W, G, M, lr: float, momentum: float, weight_decay: float,
               nesterov: bool = False, scale_coeff: float = 0.2,
               ns: Optional[Callable] = None):
@@ -180,8 +190,7 @@ def muon_step(W, G, M, lr: float, momentum: float, weight_decay: float,
     W = np.asarray(W, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
     M = np.asarray(M, dtype=np.float64)
-    M_new = momentum * M + (1.0 - momentum) * G
-    N = momentum * M_new + (1.0 - momentum) * G if nesterov else M_new
+    M_new, N = momentum_update(M, G, momentum, nesterov)
     O = ns(N)
     d_out, d_in = W.shape
     U = scale_coeff * math.sqrt(max(d_out, d_in)) * O

@@ -317,3 +317,100 @@ def test_closed_form_entries_of_a_structured_input():
     # with an explicit norm (the stored matrix's) as well
     blk2 = oracle.ns_closed_form_entries(U[rows], spec, V[cols], fro_norm=np.linalg.norm(G))
     assert np.abs(blk2 - blk).max() < 1e-12
+
+
+# ------------------------------------------------------------------ Nesterov momentum
+
+def _disjoint_diagonal_pair(n=6, m=10):
+    """Two gradients whose nonzeros sit on disjoint parts of the diagonal: every linear
+    combination of them is diagonal, so Newton-Schulz acts entry by entry on it."""
+    d1 = np.array([3.0, -1.25, 0.5])
+    d2 = np.array([-2.0, 0.75, 1.5])
+    G1, G2 = np.zeros((n, m)), np.zeros((n, m))
+    G1[[0, 1, 2], [0, 1, 2]] = d1
+    G2[[3, 4, 5], [3, 4, 5]] = d2
+    return G1, G2
+
+
+def _diagonal_ns_exact(N):
+    """sign(d) p^5(|d| / ||d||) on the diagonal of a diagonal N, the scalar map in exact
+    rational arithmetic (only the norm is a float)."""
+    d = np.diag(N)
+    nrm = np.linalg.norm(d)
+    out = np.zeros_like(N)
+    for i, di in enumerate(d):
+        if di != 0.0:
+            out[i, i] = math.copysign(float(exact_scalar_map(Fraction(abs(di) / nrm))), di)
+    return out
+
+
+def _two_step_updates(nesterov):
+    """Two Muon steps from zero momentum on the disjoint diagonal pair: returns (M2, U2)."""
+    G1, G2 = _disjoint_diagonal_pair()
+    mu = 0.9
+    ns = lambda x: oracle.ns_standard(x, eps=0.0)
+    W = np.zeros_like(G1)
+    _, M1, _ = oracle.muon_step(W, G1, np.zeros_like(G1), 0.0, mu, 0.0, nesterov=nesterov, ns=ns)
+    _, M2, U2 = oracle.muon_step(W, G2, M1, 0.0, mu, 0.0, nesterov=nesterov, ns=ns)
+    return M2, U2
+
+
+def _nesterov_pin_holds():
+    """Second step from a nonzero state: with M1 = (1 - mu) G1 the buffer is
+    M2 = mu (1 - mu) G1 + (1 - mu) G2 and the Nesterov input is
+    N2 = mu^2 (1 - mu) G1 + (1 - mu^2) G2; the update is 0.2 sqrt(10) NS(N2), entry by entry."""
+    G1, G2 = _disjoint_diagonal_pair()
+    mu = 0.9
+    M2, U2 = _two_step_updates(nesterov=True)
+    N2 = mu ** 2 * (1 - mu) * G1 + (1 - mu ** 2) * G2
+    ok_m = np.abs(M2 - (mu * (1 - mu) * G1 + (1 - mu) * G2)).max() < 1e-15
+    ok_u = np.abs(U2 - 0.2 * math.sqrt(10) * _diagonal_ns_exact(N2)).max() < 1e-13
+    return ok_m and ok_u
+
+
+def test_nesterov_momentum_two_steps_on_disjoint_diagonals():
+    assert _nesterov_pin_holds()
+
+
+def test_plain_momentum_two_steps_on_disjoint_diagonals():
+    """Without Nesterov the buffer itself is orthogonalized: N2 = M2."""
+    G1, G2 = _disjoint_diagonal_pair()
+    mu = 0.9
+    M2, U2 = _two_step_updates(nesterov=False)
+    M2_exact = mu * (1 - mu) * G1 + (1 - mu) * G2
+    assert np.abs(M2 - M2_exact).max() < 1e-15
+    assert np.abs(U2 - 0.2 * math.sqrt(10) * _diagonal_ns_exact(M2_exact)).max() < 1e-13
+    # and the two rules give different updates from this nonzero state
+    _, U2n = _two_step_updates(nesterov=True)
+    assert np.abs(U2 - U2n).max() > 1e-3
+
+
+def test_nesterov_pin_catches_a_pre_update_momentum(monkeypatch):
+    """Planted mistake: the Nesterov input formed from the buffer before its update,
+    N = mu M_old + (1 - mu) G. From zero state this still gives N proportional to G, so only
+    the nonzero-state pin above can catch it."""
+    def wrong(M, G, momentum, nesterov):
+        M_new = momentum * M + (1.0 - momentum) * G
+        N = momentum * M + (1.0 - momentum) * G if nesterov else M_new
+        return M_new, N
+    with monkeypatch.context() as mp:
+        mp.setattr(ons, "momentum_update", wrong)
+        assert not _nesterov_pin_holds()
+    assert _nesterov_pin_holds()
+
+
+def test_nesterov_input_from_a_random_nonzero_state():
+    """With the identity in place of Newton-Schulz the update exposes the orthogonalized
+    input: 0.2 sqrt(max dim) (mu (mu M + (1 - mu) G) + (1 - mu) G) with Nesterov, and
+    0.2 sqrt(max dim) (mu M + (1 - mu) G) without."""
+    rng = np.random.default_rng(45)
+    W = rng.standard_normal((7, 19))
+    G = rng.standard_normal((7, 19))
+    M = rng.standard_normal((7, 19))
+    mu = 0.95
+    s = 0.2 * math.sqrt(19)
+    _, Mn, U = oracle.muon_step(W, G, M, 0.0, mu, 0.0, nesterov=True, ns=lambda x: x)
+    assert np.abs(Mn - (mu * M + (1 - mu) * G)).max() < 1e-15
+    assert np.abs(U / s - (mu * (mu * M + (1 - mu) * G) + (1 - mu) * G)).max() < 1e-14
+    _, Mn, U = oracle.muon_step(W, G, M, 0.0, mu, 0.0, nesterov=False, ns=lambda x: x)
+    assert np.abs(U / s - (mu * M + (1 - mu) * G)).max() < 1e-14
