@@ -139,6 +139,53 @@ def describe(t) -> MnsTensor:
     return MnsTensor(t3.data_ptr(), dtype_code(t3), b, r, c, ld, stride)
 
 
+# ------------------------------------------------------------------ argument checks
+# The C ABI takes bare device pointers; these checks run before any library call so that a
+# host tensor, a mismatched dtype or a short buffer raises here instead of reaching a kernel.
+# Dtype, shape and size checks come first and device checks last.
+
+def _batch(t) -> int:
+    return t.shape[0] if t.dim() == 3 else 1
+
+
+def _check_same_shape(what, ref, **named):
+    for name, t in named.items():
+        if t is not None and tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{what}: {name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+
+
+def _check_flags(what, flags, total):
+    if flags is None:
+        return
+    torch = _torch()
+    if flags.dtype != torch.int32:
+        raise TypeError(f"{what}: flags must be int32, got {flags.dtype}")
+    if not flags.is_contiguous():
+        raise ValueError(f"{what}: flags must be contiguous")
+    if flags.numel() < total:
+        raise ValueError(f"{what}: flags holds {flags.numel()} entries, the call needs {total}")
+
+
+def _check_workspace(what, ws):
+    if ws is not None and not ws.is_contiguous():
+        raise ValueError(f"{what}: workspace must be contiguous")
+
+
+def _check_device(what, ref, **named):
+    """Every named tensor (None skipped) is a device tensor on ref's device."""
+    if not ref.is_cuda:
+        raise ValueError(f"{what}: tensors must be device tensors (got {ref.device})")
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError(f"{what}: {name} is on {t.device}, expected {ref.device}")
+
+
+def _ws_bytes(ws) -> int:
+    return ws.numel() * ws.element_size()
+
+
 def ns_params(steps: int = DEFAULT_STEPS, coeffs: Optional[Sequence] = None,
               eps: float = DEFAULT_EPS, iter_dtype: Optional[int] = None, io_dtype: int = BF16,
               restart_mask: int = STABILIZED_RESTART_MASK):
@@ -181,15 +228,20 @@ def _workspace(variant, G, params, workspace):
 
 def _ns(variant, G, out, params, workspace, flags):
     torch = _torch()
-    if not G.is_cuda:
-        raise ValueError("G must be a device tensor")
+    what = "muon_ns_batched" if variant == STANDARD else "gram_ns_batched"
+    if out is not None:
+        _check_same_shape(what, G, out=out)
+        if out.dtype != G.dtype:
+            raise TypeError(f"{what}: out must have G's dtype {G.dtype}, got {out.dtype}")
+    _check_flags(what, flags, _batch(G))
+    _check_workspace(what, workspace)
+    _check_device(what, G, out=out, flags=flags, workspace=workspace)
     out = torch.empty_like(G) if out is None else out
     ws = _workspace(variant, G, params, workspace)
     fn = _lib().muon_ns_batched if variant == STANDARD else _lib().gram_ns_batched
     fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
     _check(fn(ctypes.byref(describe(G)), ctypes.byref(describe(out)), ctypes.byref(params),
-              ctypes.c_void_p(ws.data_ptr()), ws.numel(), fptr, _stream_ptr(G)),
-           "muon_ns_batched" if variant == STANDARD else "gram_ns_batched")
+              ctypes.c_void_p(ws.data_ptr()), _ws_bytes(ws), fptr, _stream_ptr(G)), what)
     return out
 
 
@@ -214,6 +266,14 @@ def muon_step(W, G, M, *, lr: float, momentum: float, weight_decay: float,
               iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK,
               U_out=None, workspace=None, flags=None):
     """One fused Muon step (C ABI ``muon_step``); W and M are updated in place."""
+    torch = _torch()
+    what = "muon_step"
+    _check_same_shape(what, G, W=W, M=M, U_out=U_out)
+    if M.dtype != torch.float32:
+        raise TypeError(f"{what}: the momentum buffer M must be float32, got {M.dtype}")
+    _check_flags(what, flags, _batch(G))
+    _check_workspace(what, workspace)
+    _check_device(what, G, W=W, M=M, U_out=U_out, flags=flags, workspace=workspace)
     p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G),
                   restart_mask if variant == GRAM else 0)
     sp = MnsStepParams(lr, momentum, weight_decay, scale_coeff, 1 if nesterov else 0, variant)
@@ -222,8 +282,8 @@ def muon_step(W, G, M, *, lr: float, momentum: float, weight_decay: float,
     u = ctypes.byref(describe(U_out)) if U_out is not None else None
     _check(_lib().muon_step(ctypes.byref(describe(W)), ctypes.byref(describe(G)),
                             ctypes.byref(describe(M)), u, ctypes.byref(sp), ctypes.byref(p),
-                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), fptr, _stream_ptr(G)),
-           "muon_step")
+                            ctypes.c_void_p(ws.data_ptr()), _ws_bytes(ws), fptr, _stream_ptr(G)),
+           what)
     return W
 
 
@@ -246,8 +306,37 @@ def workspace_bytes_grouped(variant: int, Gs, params: MnsNsParams) -> int:
     return n.value
 
 
+def _check_groups(what, Gs, flags, workspace, **lists):
+    """Group lists of equal length (1 .. MAX_GROUPS), flags covering every matrix of every
+    group, everything on the first G's device."""
+    n = len(Gs)
+    if not 1 <= n <= MAX_GROUPS:
+        raise ValueError(f"{what}: between 1 and {MAX_GROUPS} groups, got {n}")
+    for name, ts in lists.items():
+        if ts is not None and len(ts) != n:
+            raise ValueError(f"{what}: {name} has {len(ts)} entries for {n} groups")
+    _check_flags(what, flags, sum(_batch(G) for G in Gs))
+    _check_workspace(what, workspace)
+    named = {"flags": flags, "workspace": workspace}
+    for i, G in enumerate(Gs):
+        named[f"G[{i}]"] = G
+        for name, ts in lists.items():
+            if ts is not None:
+                named[f"{name}[{i}]"] = ts[i]
+    _check_device(what, Gs[0], **named)
+
+
 def _ns_grouped(variant, Gs, outs, params, workspace, flags):
     torch = _torch()
+    what = "muon_ns_grouped" if variant == STANDARD else "gram_ns_grouped"
+    if outs is not None:
+        if len(outs) != len(Gs):
+            raise ValueError(f"{what}: outs has {len(outs)} entries for {len(Gs)} groups")
+        for i, (G, O) in enumerate(zip(Gs, outs)):
+            _check_same_shape(what, G, **{f"outs[{i}]": O})
+            if O.dtype != G.dtype:
+                raise TypeError(f"{what}: outs[{i}] must have dtype {G.dtype}, got {O.dtype}")
+    _check_groups(what, Gs, flags, workspace, outs=outs)
     outs = [torch.empty_like(G) for G in Gs] if outs is None else list(outs)
     if workspace is None:
         workspace = torch.empty(workspace_bytes_grouped(variant, Gs, params), dtype=torch.uint8,
@@ -255,8 +344,8 @@ def _ns_grouped(variant, Gs, outs, params, workspace, flags):
     fn = _lib().muon_ns_grouped if variant == STANDARD else _lib().gram_ns_grouped
     fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
     _check(fn(len(Gs), _tensor_array(Gs), _tensor_array(outs), ctypes.byref(params),
-              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), fptr, _stream_ptr(Gs[0])),
-           "muon_ns_grouped" if variant == STANDARD else "gram_ns_grouped")
+              ctypes.c_void_p(workspace.data_ptr()), _ws_bytes(workspace), fptr, _stream_ptr(Gs[0])),
+           what)
     return outs
 
 
@@ -283,6 +372,16 @@ def muon_step_grouped(Ws, Gs, Ms, *, lr: float, momentum: float, weight_decay: f
     """One fused Muon step over several batches of different shapes (C ABI
     ``muon_step_grouped``); every W and M is updated in place."""
     torch = _torch()
+    what = "muon_step_grouped"
+    for name, ts in (("Ws", Ws), ("Ms", Ms), ("U_outs", U_outs)):
+        if ts is not None and len(ts) != len(Gs):
+            raise ValueError(f"{what}: {name} has {len(ts)} entries for {len(Gs)} groups")
+    for i, G in enumerate(Gs):
+        _check_same_shape(what, G, **{f"Ws[{i}]": Ws[i], f"Ms[{i}]": Ms[i],
+                                      f"U_outs[{i}]": U_outs[i] if U_outs is not None else None})
+        if Ms[i].dtype != torch.float32:
+            raise TypeError(f"{what}: Ms[{i}] must be float32, got {Ms[i].dtype}")
+    _check_groups(what, Gs, flags, workspace, Ws=Ws, Ms=Ms, U_outs=U_outs)
     p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(Gs[0]),
                   restart_mask if variant == GRAM else 0)
     sp = MnsStepParams(lr, momentum, weight_decay, scale_coeff, 1 if nesterov else 0, variant)
@@ -293,8 +392,8 @@ def muon_step_grouped(Ws, Gs, Ms, *, lr: float, momentum: float, weight_decay: f
     u = _tensor_array(U_outs) if U_outs is not None else None
     _check(_lib().muon_step_grouped(len(Gs), _tensor_array(Ws), _tensor_array(Gs), _tensor_array(Ms),
                                     u, ctypes.byref(sp), ctypes.byref(p),
-                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), fptr,
-                                    _stream_ptr(Gs[0])), "muon_step_grouped")
+                                    ctypes.c_void_p(workspace.data_ptr()), _ws_bytes(workspace), fptr,
+                                    _stream_ptr(Gs[0])), what)
     return Ws
 
 
@@ -310,16 +409,29 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, beta1: float 
                bias_correction: bool = False):
     """One AdamW step over lists of contiguous tensors (C ABI ``adamw_step``); params and both
     fp32 moments are updated in place."""
+    torch = _torch()
     n = len(params)
     if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n) or n == 0:
         raise ValueError("params, grads and moments must be non-empty lists of equal length")
+    pdt = params[0].dtype
+    for i, (p_, g_, m_, v_) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+        if p_.dtype != pdt:
+            raise TypeError(f"adamw_step: params[{i}] is {p_.dtype}; every parameter must be {pdt}")
+        if g_.dtype != pdt:
+            raise TypeError(f"adamw_step: grads[{i}] is {g_.dtype}, its parameter is {pdt}")
+        if m_.dtype != torch.float32 or v_.dtype != torch.float32:
+            raise TypeError(f"adamw_step: the moments of tensor {i} must be float32")
+        if not (p_.numel() == g_.numel() == m_.numel() == v_.numel()):
+            raise ValueError("each parameter, gradient and moment pair must have equal sizes")
     for group in (params, grads, exp_avgs, exp_avg_sqs):
         for t in group:
             if not t.is_contiguous():
                 raise ValueError("AdamW tensors must be contiguous")
-    for p_, g_, m_, v_ in zip(params, grads, exp_avgs, exp_avg_sqs):
-        if not (p_.numel() == g_.numel() == m_.numel() == v_.numel()):
-            raise ValueError("each parameter, gradient and moment pair must have equal sizes")
+    named = {}
+    for i in range(n):
+        named.update({f"params[{i}]": params[i], f"grads[{i}]": grads[i],
+                      f"exp_avgs[{i}]": exp_avgs[i], f"exp_avg_sqs[{i}]": exp_avg_sqs[i]})
+    _check_device("adamw_step", params[0], **named)
     arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
     numels = (ctypes.c_int64 * n)(*[t.numel() for t in params])
     ap = MnsAdamwParams(lr, beta1, beta2, eps, weight_decay, step, 1 if bias_correction else 0)
@@ -346,6 +458,7 @@ def gram_trace(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAU
     """(O, trace) for the first matrix of G: the Gram iterate after each step 1 .. K-1 as a
     [K-1, n, n] fp32 tensor (C ABI ``gram_ns_trace``)."""
     torch = _torch()
+    _check_device("gram_ns_trace", G)
     G1 = G[0] if G.dim() == 3 else G
     p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G1), restart_mask)
     n = min(G1.shape)
@@ -353,7 +466,7 @@ def gram_trace(G, *, steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAU
     trace = torch.empty(steps - 1, n, n, dtype=torch.float32, device=G1.device)
     ws = _workspace(GRAM, G1, p, None)
     _check(_lib().gram_ns_trace(ctypes.byref(describe(G1)), ctypes.byref(describe(out)),
-                                 ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                 ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), _ws_bytes(ws),
                                  ctypes.c_void_p(trace.data_ptr()), _stream_ptr(G1)),
            "gram_ns_trace")
     return out, trace
