@@ -1,5 +1,5 @@
-// Shared device helpers for the gfx950 kernels: element types, loads/stores by runtime
-// dtype, and the XCD-aware workgroup remap.
+// Shared device helpers for the gfx950 kernels: element types and loads/stores by runtime
+// dtype.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +17,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __host__ __device__ inline int dtype_size(int dt) { return dt == F32 ? 4 : 2; }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
 // fp32 -> bf16, round to nearest even, NaN kept quiet with its upper payload bits: gfx950's
 // v_cvt_pk_bf16_f32, which gives exactly the bits of the bitwise definition
 // ((u + 0x7fff + lsb) >> 16, NaN -> (u >> 16) | 0x40) for every one of the 2^32 inputs.
@@ -57,16 +56,6 @@ __device__ inline void store_elem(void* p, int dt, int64_t idx, float v) {
   } else {
     reinterpret_cast<uint16_t*>(p)[idx] = dt == BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
   }
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Map the
-// hardware id so that each XCD receives a contiguous range of logical ids: consecutive
-// tiles of one matrix then share an L2.
-__device__ inline int xcd_remap(int bid, int nblocks) {
-  constexpr int NXCD = 8;
-  const int q = nblocks / NXCD, r = nblocks % NXCD;
-  const int xcd = bid % NXCD, local = bid / NXCD;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
 }  // namespace mns

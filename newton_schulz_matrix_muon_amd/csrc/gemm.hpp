@@ -57,9 +57,7 @@ struct GemmArgs {
 // group's tile list (g[i].nblocks tiles) is cut into 8 equal parts, one per XCD, so every XCD
 // gets the same share of every group (balanced whatever the groups' tile costs) and keeps
 // neighbouring tiles of a group together (shared operand panels in its L2).
-#ifndef MNS_MAXG
-#define MNS_MAXG 4
-#endif
+constexpr int MNS_MAXG = 4;
 struct GemmBatch {
   GemmArgs g[MNS_MAXG];
   int ng;
@@ -109,14 +107,8 @@ struct TileCfg {
 // Large problems: 256 x 256, 16 waves of 64 x 64, 128-byte k-stages DMA'd global -> LDS into a
 // 2-deep ring, 4 waves per SIMD (one workgroup per CU; latency is hidden by the four waves
 // each SIMD interleaves).
-#ifndef MNS_CFG128
-#define MNS_CFG128 128, 128, 2, 2, 128, 1, 2
-#endif
-#ifndef MNS_CFG256
-#define MNS_CFG256 256, 256, 4, 4, 128, 1, 4, 2
-#endif
-using Tile128 = TileCfg<MNS_CFG128>;
-using Tile256 = TileCfg<MNS_CFG256>;
+using Tile128 = TileCfg<128, 128, 2, 2, 128, 1, 2>;
+using Tile256 = TileCfg<256, 256, 4, 4, 128, 1, 4, 2>;
 
 // 8 consecutive elements of a buffer of runtime dtype (16-byte aligned for 16-bit types,
 // 32-byte for fp32).

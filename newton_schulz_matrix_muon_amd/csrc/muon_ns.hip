@@ -287,9 +287,8 @@ int resident_slots() {
   return device_cus() * per_cu;
 }
 
-#ifndef MNS_GROUP_M
-#define MNS_GROUP_M 8
-#endif
+// Tile rows a full product's tile walk covers before moving one tile column right.
+constexpr int kGroupM = 8;
 
 template <typename T, class CFG, int EPI>
 void launch_epi(int shape, dim3 grid, dim3 block, hipStream_t s, const GemmBatch& b) {
@@ -329,7 +328,7 @@ int set_tiles(const Prod& q, GemmArgs& a, int64_t batch) {
     a.tiles_m = tm;
     a.tiles_n = tn;
     a.tiles_per_mat = tm * tn;
-    a.group_m = std::max(1, std::min(tm, MNS_GROUP_M));
+    a.group_m = std::max(1, std::min(tm, kGroupM));
   }
   const int64_t nb = batch * (int64_t)a.tiles_per_mat;
   if (nb > INT32_MAX) return MNS_ERR_SHAPE;
@@ -374,16 +373,13 @@ int launch_prod(const Prod* qs, const GemmArgs* as, const int64_t* batches, int 
   });
 }
 
-// Tile choice: the 256 x 256 tile when the product is large enough to fill the chip with it.
-#ifndef MNS_TILE_POLICY
-#define MNS_TILE_POLICY 1
-#endif
+// Tile choice: the 256 x 256 tile (1) when the product is large enough to fill the chip with
+// it, else the 128 x 128 tile (0).
 int tile_choice(const Prod& q, int64_t batch) {
   const int64_t t256 = batch * ((q.M + 255) / 256) * ((q.N + 255) / 256);
-  if (MNS_TILE_POLICY == 0) return 0;
   if (q.in_dt == F32) return 0;
   if (q.M < 256 || t256 < 512) return 0;
-  return MNS_TILE_POLICY;
+  return 1;
 }
 
 GemmArgs gemm_args(const Prod& q, int64_t batch) {

@@ -28,4 +28,4 @@ def test_recorded_traffic_is_tied_to_the_kernel_sources():
         # the committed counters were taken on these sources: the bench reports them
         assert rec is not None and rec[0] > 0
     else:
-        assert rec is None
+        assert rec == (None, None)
