@@ -104,16 +104,31 @@ def bench_adamw(args):
 
 
 class ClockSampler:
-    """Samples the GPU's reported graphics clock (sysfs pp_dpm_sclk, the line marked '*')
-    every `period` seconds on a host thread, to put the MFMA peak in terms of the clock the
-    run actually had."""
+    """Samples the GPU's reported graphics clock (sysfs pp_dpm_sclk, the line marked '*') and
+    board power (hwmon power1_average or power1_input, with the power1_cap limit) every
+    `period` seconds on a host thread, to put the MFMA peak in terms of the clock the run
+    actually had and to show whether the run sat at the power limit."""
 
     def __init__(self, period: float = 0.02):
         import glob
         import threading
         paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
         self.path = paths[0] if paths else None
+        self.power_path, self.cap_w = None, None
+        if self.path:
+            dev = os.path.dirname(self.path)
+            for name in ("power1_average", "power1_input"):
+                cand = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", name)))
+                if cand:
+                    self.power_path = cand[0]
+                    cap = os.path.join(os.path.dirname(cand[0]), "power1_cap")
+                    try:
+                        self.cap_w = int(open(cap).read()) / 1e6
+                    except (OSError, ValueError):
+                        pass
+                    break
         self.samples = []
+        self.power = []
         self.period = period
         self._stop = threading.Event()
         self._t = threading.Thread(target=self._run, daemon=True)
@@ -132,6 +147,11 @@ class ClockSampler:
             v = self._read()
             if v is not None:
                 self.samples.append(v)
+            if self.power_path:
+                try:
+                    self.power.append(int(open(self.power_path).read()) / 1e6)
+                except (OSError, ValueError):
+                    pass
             self._stop.wait(self.period)
 
     def __enter__(self):
@@ -148,8 +168,13 @@ class ClockSampler:
         if not self.samples:
             return None
         xs = sorted(self.samples)
-        return {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1],
-                "samples": len(xs), "source": "sysfs pp_dpm_sclk"}
+        out = {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1],
+               "samples": len(xs), "source": "sysfs pp_dpm_sclk"}
+        if self.power:
+            ps = sorted(self.power)
+            out["power_w"] = {"median": ps[len(ps) // 2], "min": ps[0], "max": ps[-1],
+                              "cap": self.cap_w, "source": os.path.basename(self.power_path)}
+        return out
 
 
 def kernel_source_digest() -> str:
@@ -190,7 +215,7 @@ def copy_probe(mib: int):
     del src, dst
 
 
-def cpu_baseline(G_host, W_host, budget_s: float, variant: str):
+def cpu_baseline(G_host, W_host, budget_s: float, variant: str, kw: dict):
     """The fp64 oracle's Muon step on a bounded sample of the same workload (host cores)."""
     import numpy as np
     import oracle
@@ -202,8 +227,9 @@ def cpu_baseline(G_host, W_host, budget_s: float, variant: str):
     ns = (lambda x: oracle.ns_gram(x, restarts=(2,))) if variant == "gram" else oracle.ns_standard
     done, t0 = 0, time.perf_counter()
     while done < len(G_host):
-        oracle.muon_step(W_host[done], G_host[done], np.zeros_like(G_host[done]), 0.02, 0.95,
-                         0.01, nesterov=True, ns=ns)
+        oracle.muon_step(W_host[done], G_host[done], np.zeros_like(G_host[done]), kw["lr"],
+                         kw["momentum"], kw["weight_decay"], nesterov=kw["nesterov"],
+                         scale_coeff=kw["scale_coeff"], ns=ns)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -264,12 +290,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--variant", choices=["gram", "standard"], default="gram")
-    ap.add_argument("--workload", choices=["experts", "k2_full", "k2_hybrid", "adamw"], default="experts",
-                    help="experts: one batch of --batch x --rows x --cols expert matrices (default "
-                         "648 x 2048 x 7168); k2_full: the whole Kimi-K2 Muon step in one grouped call "
-                         "(432 x 2048 x 7168 up/gate, 216 x 7168 x 2048 down, 3 x 7168 x 18432 dense); "
-                         "k2_hybrid: k2_full plus AdamW on the 1-D / embedding parameters; adamw: the "
-                         "AdamW side alone")
+    ap.add_argument("--workload", choices=["experts", "experts_1408", "dense_ffn", "k2_full", "k2_hybrid",
+                                           "adamw"], default="experts",
+                    help="experts: the Kimi-K2 expert batch, --batch x --rows x --cols (default 648 x "
+                         "2048 x 7168) Gaussian plus a rank-32 spike; experts_1408: 64 x 1408 x 2048 "
+                         "low-rank (s_i = i^-0.7) plus 0.05 noise, lr 2e-4, wd 0.1; dense_ffn: 3 x 7168 x "
+                         "18432 low-rank (s_i = i^-0.5) plus 0.05 noise; k2_full: the whole Kimi-K2 Muon "
+                         "step in one grouped call (432 x 2048 x 7168 up/gate, 216 x 7168 x 2048 down, "
+                         "3 x 7168 x 18432 dense); k2_hybrid: k2_full plus AdamW on the 1-D / embedding "
+                         "parameters; adamw: the AdamW side alone")
     ap.add_argument("--batch", type=int, default=648)
     ap.add_argument("--rows", type=int, default=2048)
     ap.add_argument("--cols", type=int, default=7168)
@@ -301,9 +330,21 @@ def main():
         return bench_adamw(args)
     if args.vendor_gemm:
         return vendor_gemm(args)
+    # inputs: (generator name, workload index of the seeds) per preset
+    gen_kind, widx = "spike", 2
+    steps_kw = dict(lr=0.02, momentum=0.95, weight_decay=0.01, scale_coeff=0.2, nesterov=True)
     if args.workload == "experts":
         shapes = [(args.batch, args.rows, args.cols)]
         workload = f"kimi_k2_experts_{args.batch}x{args.rows}x{args.cols}_bf16_gaussian_plus_rank32_spike"
+    elif args.workload == "experts_1408":
+        shapes = [(64, 1408, 2048)]
+        gen_kind, widx = ("lowrank", 0.7), 1
+        steps_kw.update(lr=2e-4, weight_decay=0.1)
+        workload = "experts_64x1408x2048_bf16_powerlaw0.7_plus_noise0.05"
+    elif args.workload == "dense_ffn":
+        shapes = [(3, 7168, 18432)]
+        gen_kind, widx = ("lowrank", 0.5), 3
+        workload = "kimi_k2_dense_ffn_3x7168x18432_bf16_powerlaw0.5_plus_noise0.05"
     else:
         shapes = [(432, 2048, 7168), (216, 7168, 2048), (3, 7168, 18432)]
         workload = "kimi_k2_full_step_432x2048x7168+216x7168x2048+3x7168x18432_bf16_gaussian_plus_rank32_spike"
@@ -314,11 +355,15 @@ def main():
     total = sum(B for B, _, _ in shapes)
     Gs, Ws, Ms = [], [], []
     for i, (B, r, c) in enumerate(shapes):
-        log(f"generating {B} x {r} x {c} bf16 gradients (Gaussian + rank-32 spike)")
-        Gs.append(synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device=dev))
-        Ws.append(synth.torch_weights(B, r, c, workload_index=2, device=dev, seed_offset=500_000 + i))
+        if gen_kind == "spike":
+            log(f"generating {B} x {r} x {c} bf16 gradients (Gaussian + rank-32 spike)")
+            Gs.append(synth.torch_gaussian_plus_spike(B, r, c, workload_index=widx, device=dev))
+        else:
+            log(f"generating {B} x {r} x {c} bf16 gradients (power law i^-{gen_kind[1]} + 0.05 noise)")
+            Gs.append(synth.torch_lowrank_plus_noise(B, r, c, power=gen_kind[1], noise=0.05,
+                                                     workload_index=widx, device=dev, chunk=1 if r * c > 1 << 26 else 8))
+        Ws.append(synth.torch_weights(B, r, c, workload_index=widx, device=dev, seed_offset=500_000 + i))
         Ms.append(torch.zeros(B, r, c, dtype=torch.float32, device=dev))
-    steps_kw = dict(lr=0.02, momentum=0.95, weight_decay=0.01, scale_coeff=0.2, nesterov=True)
 
     p_g = ops.ns_params(io_dtype=ops.BF16, restart_mask=1 << 2)
     p_s = ops.ns_params(io_dtype=ops.BF16, restart_mask=0)
@@ -332,7 +377,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        k = min(shapes[0][0], 24)     # bounded sample: the oracle stops after --cpu-budget seconds
+        # bounded sample: the oracle stops after --cpu-budget seconds (one matrix at least, which
+        # for the 7168 x 18432 dense matrices is already ~30 s of host work)
+        k = 1 if shapes[0][1] * shapes[0][2] > 1 << 26 else min(shapes[0][0], 24)
         Gh = Gs[0][:k].double().cpu().numpy()
         Wh = Ws[0][:k].double().cpu().numpy()
 
@@ -446,14 +493,14 @@ def main():
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(Gh, Wh, args.cpu_budget, args.variant)
+        cpu = cpu_baseline(Gh, Wh, args.cpu_budget, args.variant, steps_kw)
 
     config = {"workload": workload,
               "groups": [{"batch": B, "rows": r, "cols": c} for B, r, c in shapes],
               "step": f"fused Muon step, {args.variant} Newton-Schulz K=5"
                       + (" (fp16 iterates, restart after step 2)" if args.variant == "gram" else ""),
-              "lr": 0.02, "momentum": 0.95, "nesterov": True, "weight_decay": 0.01,
-              "scale": "0.2*sqrt(max(rows, cols))"}
+              "lr": steps_kw["lr"], "momentum": steps_kw["momentum"], "nesterov": steps_kw["nesterov"],
+              "weight_decay": steps_kw["weight_decay"], "scale": "0.2*sqrt(max(rows, cols))"}
     if len(shapes) == 1:
         config.update(batch=shapes[0][0], rows=shapes[0][1], cols=shapes[0][2])
     out = {
@@ -467,7 +514,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 io, fp16 iterates",
         "data": "synthetic",
         "config": config,
         "effective_tflops": variants[args.variant]["algorithmic_tflops"],
