@@ -59,6 +59,11 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m newton_schulz_matrix_muon_amd.build`")
+        # torch carries its own HIP runtime (soname libamdhip64.so.7). Loading it first makes
+        # the library bind to that same runtime; loaded the other way round, the library would
+        # pull in the system runtime and the process would hold two, and the library's one
+        # would not see the device torch's tensors and streams live on.
+        _torch()
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         vp, sz = ctypes.c_void_p, ctypes.c_size_t

@@ -231,3 +231,20 @@ def test_adamw_argument_errors(L):
     assert f(a=[P(0x1000, 0), P(0x2000, 0xa000), P(0x3000, 0xb000), P(0x4000, 0xc000)]) == -1            # null
     assert f(nn=(ctypes.c_int64 * 2)(100, -1)) == -1
     assert L.mns_last_hip_error() == 0
+
+
+def test_binding_and_torch_share_one_hip_runtime():
+    """Loading the library through the binding, even before the caller imports torch, leaves
+    exactly one HIP runtime in the process (torch's), so the library's calls see the device and
+    the streams torch uses."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from newton_schulz_matrix_muon_amd import ops\n"
+            "ops.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         check=True).stdout
+    assert out.strip().splitlines()[-1] == "1"
