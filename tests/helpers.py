@@ -58,3 +58,22 @@ def w_update_ok(Wg, W_prev, Ug, lr, wd, dtype="bf16"):
     else:
         ok = np.abs(Wg - w_exp) <= slack + np.spacing(np.abs(w_exp).astype(np.float32)).astype(np.float64)
     return bool(ok.all()), float(np.mean(~ok))
+
+
+def gram_singular_range(O):
+    """(min, max) singular value of an n x m matrix (n <= m) from the eigenvalues of the n x n
+    Gram matrix O O^T in fp64 (much cheaper than an SVD at n x m = 7168 x 18432)."""
+    O = np.asarray(O, dtype=np.float64)
+    if O.shape[0] > O.shape[1]:
+        O = O.T
+    ev = np.linalg.eigvalsh(O @ O.T)
+    s = np.sqrt(np.clip(ev, 0.0, None))
+    return float(s.min()), float(s.max())
+
+
+def band_ok_gram(got, ref, tol, ref_range=None):
+    """band_ok through gram_singular_range; ref_range may carry the reference's precomputed
+    (lo, hi)."""
+    lo, hi = gram_singular_range(ref) if ref_range is None else ref_range
+    gmin, gmax = gram_singular_range(got)
+    return bool(gmin >= lo - tol * hi and gmax <= hi + tol * hi), (lo, hi, gmin, gmax)

@@ -133,11 +133,12 @@ def test_grouped_k2_structure_reduced(torch, ops):
     assert math.isfinite(float(outs[0].float().abs().max()))
 
 
+@pytest.mark.timeout(900)
 def test_grouped_k2_full_size_equals_single_calls(torch, ops):
     """The whole Kimi-K2 Muon step's matrices at full size in one grouped call (432 x 2048 x
     7168 up/gate, 216 x 7168 x 2048 down, 3 x 7168 x 18432 dense): the 256 x 256 kernels with
     every group's tiles split over the XCDs, bit for bit equal to one call per group; the first
-    matrix of the two expert groups against the oracle."""
+    matrix of every group (the dense one included) against the oracle."""
     say("case grouped K2 full size")
     shapes = [(432, 2048, 7168), (216, 7168, 2048), (3, 7168, 18432)]
     Gs = [synth.torch_gaussian_plus_spike(b, r, c, workload_index=2, device="cuda") for b, r, c in shapes]
@@ -148,7 +149,7 @@ def test_grouped_k2_full_size_equals_single_calls(torch, ops):
         torch.cuda.synchronize()
         assert torch.equal(O, S)
         del S
-    for i in (0, 1):
+    for i in (0, 1, 2):
         e = rel_fro(to_np(outs[i][0]), oracle.ns_gram(to_np(Gs[i][0]), restarts=(2,)))
         say(f"  group {i} matrix 0: rel_F {e:.3e}")
         assert e < TOL

@@ -4,8 +4,9 @@
   wd 0.1, scale 0.2 sqrt(2048)); sampled matrices checked against the oracle.
 * Kimi-K2 expert batch 648 x 2048 x 7168 bf16 (the bench's workload, whole batch in one
   workspace chunk): sampled matrices against the oracle for both variants.
-* Kimi-K2 dense 3 x 7168 x 18432 bf16: a power-law input with a known SVD built from
-  Kronecker products of small orthogonal factors; sampled output entries against the
+* Kimi-K2 dense 3 x 7168 x 18432 bf16: its own seeded input (power law i^-0.5 plus 0.05
+  noise) against the oracle element by element, and a power-law input with a known SVD built
+  from Kronecker products of small orthogonal factors, sampled output entries against the
   closed form U p(S) V^T (a property that holds at any size).
 """
 import math
@@ -15,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import band_ok, bf16_steps, rel_fro, say, to_np, w_update_ok
+from helpers import band_ok, band_ok_gram, bf16_steps, gram_singular_range, rel_fro, say, to_np, w_update_ok
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -77,6 +78,61 @@ def test_expert_batch_1408x2048_muon_step(torch, ops, variant):
             Wh[b], Mh[b] = Wg, Mg
 
 
+# Matrices on both sides of the boundaries where the persistent tile walk of the 648-matrix
+# batch hands over from one XCD's share of the tile list to the next (648 / 8 = 81 matrices per
+# share), plus the first and the last matrix.
+K2_PICKS = [0, 80, 81, 161, 162, 323, 324, 647]
+
+
+def w_frobenius_bound_ok(Wg, Wn, Un, lr, tol):
+    """W after a step, against the oracle's fp64 W: the GPU's W is the exact update rounded once
+    to bf16 with its own U, so ||W_gpu - W_oracle||_F <= ||half a bf16 step of W||_F +
+    lr ||U_gpu - U_oracle||_F, and the second term is at most lr tol ||U_oracle||_F when U meets
+    the tolerance. Returns (ok, lhs, rhs)."""
+    big = np.maximum(np.abs(Wn), np.abs(Wg)).astype(np.float32)
+    half_ulp = 0.5 * np.spacing(big).astype(np.float64) * 2 ** 16
+    lhs = float(np.linalg.norm(Wg - Wn))
+    rhs = float(np.linalg.norm(half_ulp) + lr * tol * np.linalg.norm(Un)) * (1 + 1e-6)
+    return lhs <= rhs, lhs, rhs
+
+
+def test_k2_expert_batch_timed_muon_step(torch, ops):
+    """The exact call the bench times: muon_step over 648 x 2048 x 7168 bf16 with stabilized
+    Gram NS, Nesterov momentum, bf16 W, fp32 M, the bench's workspace, no U_out and no flags
+    (so the last product updates W in its typed weight-update epilogue on the persistent
+    grid). Two steps, the second from the nonzero momentum the first left; W and M of the
+    matrices at the XCD-share boundaries against the oracle's Muon step."""
+    B, r, c = 648, 2048, 7168
+    say(f"case k2 experts {B}x{r}x{c}: timed muon_step call, generating")
+    G1 = synth.torch_gaussian_plus_spike(B, r, c, workload_index=2, device="cuda")
+    G2 = synth.torch_gaussian_plus_spike(B, r, c, workload_index=12, device="cuda")
+    W = synth.torch_weights(B, r, c, workload_index=2, device="cuda", seed_offset=500_000)
+    M = torch.zeros(B, r, c, dtype=torch.float32, device="cuda")
+    p_g = ops.ns_params(io_dtype=ops.BF16, restart_mask=1 << 2)
+    p_s = ops.ns_params(io_dtype=ops.BF16, restart_mask=0)
+    ws = torch.empty(max(ops.workspace_bytes(ops.GRAM, G1, p_g),
+                         ops.workspace_bytes(ops.STANDARD, G1, p_s)), dtype=torch.uint8, device="cuda")
+    kw = dict(lr=0.02, momentum=0.95, weight_decay=0.01, scale_coeff=0.2, nesterov=True)
+    ns = lambda x: oracle.ns_gram(x, restarts=(2,))
+    Wh = {b: to_np(W[b]) for b in K2_PICKS}
+    Mh = {b: np.zeros((r, c)) for b in K2_PICKS}
+    for step, G in enumerate((G1, G2)):
+        say(f"  step {step}: muon_step on the whole batch")
+        ops.muon_step(W, G, M, variant=ops.GRAM, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        for b in K2_PICKS:
+            Wn, Mn, Un = oracle.muon_step(Wh[b], to_np(G[b]), Mh[b], kw["lr"], kw["momentum"],
+                                          kw["weight_decay"], nesterov=True, scale_coeff=0.2, ns=ns)
+            Wg, Mg = to_np(W[b]), to_np(M[b])
+            ok, lhs, rhs = w_frobenius_bound_ok(Wg, Wn, Un, kw["lr"], TOL)
+            em = rel_fro(Mg, Mn)
+            say(f"    matrix {b}: ||W - W_oracle||_F {lhs:.4e} (bound {rhs:.4e}), M rel_F {em:.2e}")
+            assert ok
+            assert em < 1e-6
+            assert bool(torch.isfinite(W[b].float()).all())
+            Wh[b], Mh[b] = Wg, Mg
+
+
 def test_k2_expert_batch_648x2048x7168_sampled(torch, ops):
     B, r, c = 648, 2048, 7168
     say(f"case k2 experts {B}x{r}x{c}: generating")
@@ -87,7 +143,7 @@ def test_k2_expert_batch_648x2048x7168_sampled(torch, ops):
                          ops.workspace_bytes(ops.STANDARD, G, p_s)), dtype=torch.uint8, device="cuda")
     O = torch.empty_like(G)
     flags = torch.full((B,), -1, dtype=torch.int32, device="cuda")
-    picks = [0, 647]
+    picks = K2_PICKS
     Gh = {b: to_np(G[b]) for b in picks}
     for variant in ("gram_stabilized", "standard"):
         say(f"  running {variant} on the whole batch")
@@ -107,6 +163,68 @@ def test_k2_expert_batch_648x2048x7168_sampled(torch, ops):
             ok, info = band_ok(got, ref, TOL)
             say(f"  {variant} matrix {b}: rel_F {e:.3e}, band {info}")
             assert e <= TOL and ok
+
+
+@pytest.fixture(scope="module")
+def dense_ffn(torch):
+    """The dense FFN batch as the bench generates it: 3 x 7168 x 18432 bf16, U diag(i^-0.5) V^T
+    plus 0.05 N(0, 1) noise, normalised. The fp64 reference of matrix 0 (the oracle's stabilized
+    Gram iteration on the stored bf16 values; in fp64 the standard and Gram forms agree to
+    ~1e-12, which the oracle's own tests pin) and its singular-value range are computed once."""
+    n, m = 7168, 18432
+    say(f"case k2 dense 3x{n}x{m} power law + noise: generating")
+    G = synth.torch_lowrank_plus_noise(3, n, m, power=0.5, noise=0.05, workload_index=3,
+                                       device="cuda", chunk=1)
+    G0 = to_np(G[0])
+    say("  oracle on matrix 0 (fp64, host)")
+    ref = oracle.ns_gram(G0, restarts=(2,))
+    rng_ = gram_singular_range(ref)
+    return G, ref, rng_
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant", ["gram_stabilized", "standard"])
+def test_k2_dense_3x7168x18432_own_input(torch, ops, dense_ffn, variant):
+    """The dense FFN batch on its own input, in the bench's launch configuration (all three
+    matrices in one call): matrix 0 against the fp64 oracle element by element (relative
+    Frobenius error) and the band of its singular values."""
+    G, ref, ref_range = dense_ffn
+    say(f"  dense FFN {variant}")
+    flags = torch.zeros(3, dtype=torch.int32, device="cuda")
+    O = ops.gram_ns(G, flags=flags) if variant != "standard" else ops.muon_ns(G, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.abs().sum()) == 0
+    assert bool(torch.isfinite(O.float()).all())
+    got = to_np(O[0])
+    e = rel_fro(got, ref)
+    ok, info = band_ok_gram(got, ref, TOL, ref_range)
+    say(f"  {variant} matrix 0: rel_F {e:.3e}, band {info}")
+    assert e <= TOL and ok
+
+
+@pytest.mark.parametrize("variant", ["standard", "gram_stabilized"])
+def test_expert_batch_1408x2048_bf16_iterates(torch, ops, variant):
+    """The expert batch with every iterate stored in bf16 (64 x 1408 x 2048, the input as the
+    workload defines it), NS alone on the whole batch; sampled matrices against the oracle.
+    The library's default for bf16 input keeps the normalised iterates in fp16."""
+    say(f"case expert 64x1408x2048 bf16 iterates {variant}")
+    B, r, c = 64, 1408, 2048
+    G = synth.torch_lowrank_plus_noise(B, r, c, power=0.7, noise=0.05, workload_index=1,
+                                       device="cuda")
+    if variant == "standard":
+        O = ops.muon_ns(G, iter_dtype=ops.BF16)
+        ns = oracle.ns_standard
+    else:
+        O = ops.gram_ns(G, iter_dtype=ops.BF16)
+        ns = lambda x: oracle.ns_gram(x, restarts=(2,))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O.float()).all())
+    for b in (0, 37, 63):
+        ref = ns(to_np(G[b]))
+        e = rel_fro(to_np(O[b]), ref)
+        ok, info = band_ok(to_np(O[b]), ref, TOL)
+        say(f"  matrix {b}: rel_F {e:.3e}, band {info}")
+        assert e <= TOL and ok
 
 
 def test_k2_dense_3x7168x18432_structured(torch, ops):
