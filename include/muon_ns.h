@@ -161,6 +161,28 @@ MNS_API int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor
               void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
 /*
+ * muon_step without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). The scratch
+ * space is a static device array of MNS_NOALLOC_SCRATCH_BYTES compiled into the library; each
+ * GPU the library runs on holds its own copy from the library's first use on that GPU until
+ * the process ends. The batch is processed in the largest chunks whose workspace fits it (as
+ * muon_step does with a workspace of that size, which gives identical results). The call
+ * allocates and frees nothing.
+ * Arguments and results as for muon_step, without ws / ws_bytes.
+ * Errors: as for muon_step, and MNS_ERR_WORKSPACE when one matrix alone needs more scratch
+ * than MNS_NOALLOC_SCRATCH_BYTES (returned before any HIP call; e.g. a 2048 x 7168 matrix
+ * needs ~100 MB with stabilized Gram NS, a 7168 x 18432 one ~1 GB). The first call on a GPU
+ * looks up that GPU's copy of the array (MNS_ERR_HIP if the lookup fails).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads without ordering) race on it and must not be
+ * issued; calls ordered on one stream are safe. No part of the array needs to start zeroed.
+ */
+#define MNS_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+MNS_API int muon_step_noalloc(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
+                      const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
+                      int32_t* flags, void* stream);
+
+/*
  * Grouped calls: ngroups (1 .. 4) strided batches of different shapes in one call, e.g. the
  * Kimi-K2 optimizer step of the Gram Newton-Schulz article's timing (expert up/gate matrices,
  * expert down matrices in the transposed orientation, and the dense FFN matrices). Every group

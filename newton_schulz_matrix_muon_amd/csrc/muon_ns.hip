@@ -22,6 +22,10 @@
 
 using namespace mns;
 
+// Scratch space of muon_step_noalloc. In host code this name is only the handle that
+// hipGetSymbolAddress resolves to the current GPU's copy; kernels receive that address.
+static __device__ __align__(256) char scratch[MNS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip = 0;
@@ -926,6 +930,38 @@ bool any_overlap(const mns_tensor* const* t, int n) {
   return false;
 }
 
+// Device address of the GPU's copy of `scratch` for work on `stream`, looked up once per GPU
+// with that GPU current.
+int scratch_address(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0, cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess) e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return MNS_ERR_HIP;
+  }
+  if (dev < 0 || dev >= 64) return MNS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) {
+      g_last_hip = (int)e;
+      return MNS_ERR_HIP;
+    }
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || !a || back != hipSuccess) {
+      g_last_hip = (int)(e != hipSuccess ? e : back);
+      return MNS_ERR_HIP;
+    }
+    addr[dev] = a;
+  }
+  *out = addr[dev];
+  return MNS_OK;
+}
+
 int run_adamw(int nt, void* const* params, const void* const* grads, float* const* m, float* const* v,
               const int64_t* numels, int dt, const mns_adamw_params* ap, hipStream_t s) {
   AdamTable t;
@@ -1009,6 +1045,24 @@ int muon_step(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M, con
   FinalOut fo;
   step_io(W, G, M, U_out, sp, &src, &fo);
   return run_ns(sp->variant, src, fo, c, ws, ws_bytes, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+int muon_step_noalloc(const mns_tensor* W, const mns_tensor* G, const mns_tensor* M,
+                      const mns_tensor* U_out, const mns_step_params* sp, const mns_ns_params* p,
+                      int32_t* flags, void* stream) {
+  if (int st = check_step(W, G, M, U_out)) return st;
+  if (int st = check_step_params(sp)) return st;
+  NsConf c;
+  if (int st = check_params(p, G->dtype, &c, G, 1)) return st;
+  const size_t cap = MNS_NOALLOC_SCRATCH_BYTES;
+  if (pick_chunk(sp->variant, geometry(G), c, G->batch, cap) < 1) return MNS_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (int st = scratch_address(s, &ws)) return st;
+  Source src;
+  FinalOut fo;
+  step_io(W, G, M, U_out, sp, &src, &fo);
+  return run_ns(sp->variant, src, fo, c, ws, cap, flags, s);
 }
 
 int mns_workspace_bytes_grouped(int variant, int ngroups, const mns_tensor* G, const mns_ns_params* p,

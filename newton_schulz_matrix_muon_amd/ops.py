@@ -73,6 +73,8 @@ def _lib():
             fn.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
         lib.muon_step.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
                                   P(MnsStepParams), P(MnsNsParams), vp, sz, vp, vp]
+        lib.muon_step_noalloc.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
+                                          P(MnsStepParams), P(MnsNsParams), vp, vp]
         lib.gram_ns_trace.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
         lib.mns_workspace_bytes_grouped.argtypes = [ctypes.c_int, ctypes.c_int, P(MnsTensor),
                                                     P(MnsNsParams), P(sz)]
@@ -98,7 +100,7 @@ def _lib():
         for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched, lib.gram_ns_trace,
                   lib.mns_workspace_bytes_grouped, lib.muon_ns_grouped, lib.gram_ns_grouped,
                   lib.muon_step_grouped,
-                  lib.muon_step, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
+                  lib.muon_step, lib.muon_step_noalloc, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
                   lib.mns_timing_reset, lib.mns_timing_query, lib.mns_timing_kinds):
             f.restype = ctypes.c_int
         _LIB = lib
@@ -289,6 +291,35 @@ def muon_step(W, G, M, *, lr: float, momentum: float, weight_decay: float,
                             ctypes.byref(describe(M)), u, ctypes.byref(sp), ctypes.byref(p),
                             ctypes.c_void_p(ws.data_ptr()), _ws_bytes(ws), fptr, _stream_ptr(G)),
            what)
+    return W
+
+
+# Size of the static device scratch behind muon_step_noalloc (MNS_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def muon_step_noalloc(W, G, M, *, lr: float, momentum: float, weight_decay: float,
+                      scale_coeff: float = 0.2, nesterov: bool = False, variant: int = GRAM,
+                      steps: int = DEFAULT_STEPS, coeffs=None, eps: float = DEFAULT_EPS,
+                      iter_dtype: Optional[int] = None, restart_mask: int = STABILIZED_RESTART_MASK,
+                      U_out=None, flags=None):
+    """One fused Muon step without a workspace (C ABI ``muon_step_noalloc``: the library's
+    static device scratch); W and M are updated in place."""
+    torch = _torch()
+    what = "muon_step_noalloc"
+    _check_same_shape(what, G, W=W, M=M, U_out=U_out)
+    if M.dtype != torch.float32:
+        raise TypeError(f"{what}: the momentum buffer M must be float32, got {M.dtype}")
+    _check_flags(what, flags, _batch(G))
+    _check_device(what, G, W=W, M=M, U_out=U_out, flags=flags)
+    p = ns_params(steps, coeffs, eps, iter_dtype, dtype_code(G),
+                  restart_mask if variant == GRAM else 0)
+    sp = MnsStepParams(lr, momentum, weight_decay, scale_coeff, 1 if nesterov else 0, variant)
+    fptr = ctypes.c_void_p(flags.data_ptr()) if flags is not None else None
+    u = ctypes.byref(describe(U_out)) if U_out is not None else None
+    _check(_lib().muon_step_noalloc(ctypes.byref(describe(W)), ctypes.byref(describe(G)),
+                                    ctypes.byref(describe(M)), u, ctypes.byref(sp), ctypes.byref(p),
+                                    fptr, _stream_ptr(G)), what)
     return W
 
 

@@ -233,6 +233,27 @@ def test_adamw_argument_errors(L):
     assert L.mns_last_hip_error() == 0
 
 
+def test_noalloc_step_rejects_a_matrix_larger_than_its_scratch(L):
+    """muon_step_noalloc checks that one matrix fits the static scratch before any HIP call
+    (the pointers here are not device memory): a 7168 x 18432 matrix needs ~1 GB of scratch
+    with stabilized Gram NS and is refused; argument errors come first as in muon_step."""
+    from newton_schulz_matrix_muon_amd import ops
+    p = ops.ns_params(io_dtype=ops.BF16)
+    sp = ops.MnsStepParams(0.02, 0.95, 0.01, 0.2, 1, ops.GRAM)
+    big = dict(batch=1, rows=7168, cols=18432)
+    W = _t(ops, ptr=0x10000000000, **big)
+    G = _t(ops, ptr=0x20000000000, **big)
+    M = _t(ops, ptr=0x30000000000, dtype=0, **big)
+    call = lambda w, g, m, s=sp: L.muon_step_noalloc(ctypes.byref(w), ctypes.byref(g), ctypes.byref(m),
+                                                     None, ctypes.byref(s), ctypes.byref(p), None, None)
+    assert call(W, G, M) == -4
+    assert call(W, G, _t(ops, ptr=0x30000000000, **big)) == -2        # M not fp32
+    assert call(W, _t(ops, ptr=0, **big), M) == -1                     # null input
+    bad = ops.MnsStepParams(float("inf"), 0.95, 0.01, 0.2, 1, ops.GRAM)
+    assert call(W, G, M, bad) == -1
+    assert L.mns_last_hip_error() == 0
+
+
 def test_binding_and_torch_share_one_hip_runtime():
     """Loading the library through the binding, even before the caller imports torch, leaves
     exactly one HIP runtime in the process (torch's), so the library's calls see the device and
