@@ -315,6 +315,10 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt on the LDS / scalar-memory counter only (lgkmcnt(0); vmcnt and expcnt at their
+// no-wait maxima).
+__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // Value known to be equal across the wave (kept in scalar registers).
 __device__ inline int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -329,6 +333,15 @@ __device__ inline void barrier_nofence() {
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ __volatile__("" ::: "memory");
+}
+
+// Empty asm that "modifies" the fragment registers: MFMAs that read them cannot move above it.
+template <typename T, int TM, int TN>
+__device__ inline void pin_frags(typename Frag<T>::type (&a)[TM], typename Frag<T>::type (&b)[TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) __asm__ __volatile__("" : "+v"(a[i]));
+#pragma unroll
+  for (int j = 0; j < TN; ++j) __asm__ __volatile__("" : "+v"(b[j]));
 }
 
 template <typename T, int TM, int TN>
@@ -561,7 +574,7 @@ gemm_nt_kernel(const GemmBatch gb) {
   __shared__ __attribute__((aligned(16))) char lds[CFG::LDS];
 
   // the wave index is uniform across a wave: keep it (and everything derived) in SGPRs
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+  const int tid = threadIdx.x, lane0 = tid & 63, wave = wave_uniform(tid >> 6);
   const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
 
   // Persistent: each workgroup walks a strided sequence of tiles inside its XCD's contiguous
@@ -575,6 +588,10 @@ gemm_nt_kernel(const GemmBatch gb) {
   for (int g = 0; g < gb.ng; ++g)
     xtiles += xcd_part_lo(gb.g[g].nblocks, xcd + 1) - xcd_part_lo(gb.g[g].nblocks, xcd);
   for (int j = wgx; j < xtiles; j += per_xcd) {
+  // the lane's offsets are recomputed for every tile instead of being kept across tiles
+  int lane_t = lane0;
+  __asm__ __volatile__("" : "+v"(lane_t));
+  const int lane = lane_t;
   int gi = 0, jj = j;
   for (;;) {
     const int ps = xcd_part_lo(gb.g[gi].nblocks, xcd + 1) - xcd_part_lo(gb.g[gi].nblocks, xcd);
@@ -688,27 +705,43 @@ gemm_nt_kernel(const GemmBatch gb) {
     wait_stages(min(PD, nk) - 1);
     barrier_nofence();
     for (int kt = 0; kt < nk; ++kt) {
+      // the previous stage's last k-group, whose fragments were read before the barrier: these
+      // MFMAs keep the pipe busy while this stage's first fragments are read
+      if (kt > 0) mma<T, TM, TN>(fa, fb, acc);
       if (kt + PD < nk) issue(kt + PD);
       const char* sb = lds + (kt % NST) * CFG::STG;
       const char* As = sb + (wm * WTM) * KB;
       const char* Bs = sb + (BM + wn * WTN) * KB;
+      // fragment addresses are recomputed every stage instead of being kept per stage slot
+      int swv = sw;
+      __asm__ __volatile__("" : "+v"(swv));
+      int boffv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        boffv[j] = boff[j];
+        __asm__ __volatile__("" : "+v"(boffv[j]));
+      }
 #pragma unroll
       for (int g = 0; g < CFG::NG; ++g) {
         if constexpr (BKM && ES == 2) {
-          load_frags_dl<T, TM, TN, KB, false>(As, Bs, lane, g, sw, fa, fb);
-          load_b_kmajor<T, TN, BN * ES>(sb + BM * KB, boff, g, fb);
+          load_frags_dl<T, TM, TN, KB, false>(As, Bs, lane, g, swv, fa, fb);
+          load_b_kmajor<T, TN, BN * ES>(sb + BM * KB, boffv, g, fb);
         } else if constexpr (BKM) {
-          load_frags_dl<T, TM, TN, KB, false>(As, Bs, lane, g, sw, fa, fb);
+          load_frags_dl<T, TM, TN, KB, false>(As, Bs, lane, g, swv, fa, fb);
           load_b_kmajor_f32<TN, BN * ES>(sb + BM * KB, lane, wn * WTN, g, fb);
         } else {
-          load_frags_dl<T, TM, TN, KB>(As, Bs, lane, g, sw, fa, fb);
+          load_frags_dl<T, TM, TN, KB>(As, Bs, lane, g, swv, fa, fb);
         }
-        mma<T, TM, TN>(fa, fb, acc);
+        if (g + 1 < CFG::NG) mma<T, TM, TN>(fa, fb, acc);
       }
+      // the deferred fragments must be in registers before the next DMA refills their slot
+      wait_lgkmcnt0();
       // stage kt + 1 must have landed; stages kt + 2 .. min(kt + PD, nk - 1) may be in flight
       if (kt + 1 < nk) wait_stages(min(kt + PD, nk - 1) - (kt + 1));
       barrier_nofence();
+      pin_frags<T, TM, TN>(fa, fb);
     }
+    mma<T, TM, TN>(fa, fb, acc);
   } else {
   // Global -> register staging, 16-byte chunks: chunk c = tid + NT q covers staged row
   // c / CPR, bytes 16 (c % CPR) .. +15. Row offsets are fixed per thread; rows past the end
