@@ -162,6 +162,16 @@ __device__ inline void store_part(void* p, int dt, int64_t idx, const float (&v)
 // Typed 8-element vector load/store (16-bit types: one 16-byte access; fp32: two).
 template <typename OT> struct VecIO;
 template <> struct VecIO<float> {
+  typedef float raw __attribute__((ext_vector_type(8)));
+  static __device__ inline raw load_raw(const void* p, int64_t idx) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + idx);
+    const f32x4 a = q[0], b = q[1];
+    return raw{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  static __device__ inline void unpack(const raw& w, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = w[e];
+  }
   static __device__ inline void load(const void* p, int64_t idx, float (&v)[8]) {
     const f32x4* q = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + idx);
     const f32x4 a = q[0], b = q[1];
@@ -181,14 +191,18 @@ template <typename H> struct VecIO16 {
   static __device__ inline uint32_t bits(float f) {
     if constexpr (__is_same(H, __bf16)) return f32_to_bf16_bits(f); else return f32_to_f16_bits(f);
   }
-  static __device__ inline void load(const void* p, int64_t idx, float (&v)[8]) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p) + idx);
+  typedef u32x4 raw;
+  static __device__ inline raw load_raw(const void* p, int64_t idx) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p) + idx);
+  }
+  static __device__ inline void unpack(const raw& w, float (&v)[8]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[2 * e] = cvt((uint16_t)(w[e] & 0xffffu));
       v[2 * e + 1] = cvt((uint16_t)(w[e] >> 16));
     }
   }
+  static __device__ inline void load(const void* p, int64_t idx, float (&v)[8]) { unpack(load_raw(p, idx), v); }
   static __device__ inline void store(void* p, int64_t idx, const float (&v)[8]) {
     u32x4 w;
 #pragma unroll
@@ -377,15 +391,35 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Accumulators of this wave to the fp32 epilogue slab (its rows from lrow0 of the slab).
+template <class CFG>
+__device__ inline void acc_to_slab(float* Cs, const f32x16 (&acc)[CFG::TM][CFG::TN], int lane, int wn, int lrow0) {
+  constexpr int CP = CFG::CP;
+  float* base = Cs + (lrow0 + 4 * (lane >> 5)) * CP + wn * CFG::WTN + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < CFG::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < CFG::TN; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) base[(i * 32 + 8 * (rr >> 2) + (rr & 3)) * CP + j * 32] = acc[i][j][rr];
+}
+
+// Barrier between epilogue passes: only this workgroup's LDS accesses need to be complete (the
+// slab is rewritten by the next pass or the next tile's DMA); its global stores stay in flight.
+__device__ inline void lds_barrier() {
+  wait_lgkmcnt0();
+  barrier_nofence();
+}
+
 // Fast epilogue for internal outputs: C (row-major; mirrored for symmetric results) and
 // optionally C^T, both of dtype OT with rows padded to multiples of 8, E of dtype ET. No
 // runtime dtype dispatch and whole 16-byte vectors only.
 template <typename OT, typename ET, bool TRI, class CFG>
 __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)[CFG::TM][CFG::TN],
-                                     int mat, int ti, int tj, int row0, int col0) {
-  constexpr int BN = CFG::BN, NT = CFG::NT, WTM = CFG::WTM, WTN = CFG::WTN, CP = CFG::CP;
-  constexpr int TM = CFG::TM, TN = CFG::TN, SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                     int mat, int ti, int tj, int row0, int col0, int lane) {
+  constexpr int BN = CFG::BN, NT = CFG::NT, WTM = CFG::WTM, CP = CFG::CP;
+  constexpr int SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
+  const int wave = wave_uniform(threadIdx.x >> 6), tid = wave * 64 + lane;
   const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
   float sc = 1.f;
   if (p.spow) {
@@ -402,21 +436,23 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
   float* Cs = reinterpret_cast<float*>(lds);
   for (int sl = 0; sl < CFG::WVM / SR; ++sl) {
     if (wm / SR == sl) {
-      const int lrow0 = (wm % SR) * WTM;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int r = lrow0 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            const int c = wn * WTN + j * 32 + (lane & 31);
-            Cs[r * CP + c] = acc[i][j][rr];
-          }
+      acc_to_slab<CFG>(Cs, acc, lane, wn, (wm % SR) * WTM);
     }
-    __syncthreads();
+    lds_barrier();
     const int srow0 = row0 + sl * SROWS;
-    for (int idx = tid; idx < SROWS * VPR; idx += NT) {
+    // E vector of element index i (8 values from row srow0 + i / VPR): issued one vector ahead
+    // of its use, into two fixed registers, so that its wait does not also wait for the stores
+    // issued in between. Every fetch is issued and used (a vector outside E reads E's first
+    // vector and is discarded), so no path leaves a load in flight.
+    constexpr int ITR = SROWS * VPR / NT;
+    static_assert(ITR % 2 == 0 && ITR * NT == SROWS * VPR, "row pass in pairs of iterations");
+    auto fetch_e = [&](int i, typename VecIO<ET>::raw& e) {
+      const int r = srow0 + i / VPR, c = col0 + (i % VPR) * 8;
+      const bool h = r < p.e_rows && c < p.e_cols;
+      e = VecIO<ET>::load_raw(Eb, h ? (int64_t)r * p.lde + c : 0);
+      return h;
+    };
+    auto row_vec = [&](int idx, const typename VecIO<ET>::raw* er, bool he) {
       const int lr = idx / VPR, lc = (idx - lr * VPR) * 8;
       const int r = srow0 + lr, c = col0 + lc;
       float* cs = Cs + lr * CP + lc;
@@ -425,11 +461,11 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
       float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] *= c2;
-      if (Eb && r < p.e_rows && c < p.e_cols) {
+      if (er) {
         float ev[8];
-        VecIO<ET>::load(Eb, (int64_t)r * p.lde + c, ev);
+        VecIO<ET>::unpack(*er, ev);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += c1 * ev[e];
+        for (int e = 0; e < 8; ++e) v[e] = he ? v[e] + c1 * ev[e] : v[e];
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -449,9 +485,24 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
             if (c + e >= r) store_elem(Cb, sizeof(OT) == 4 ? F32 : (__is_same(OT, __bf16) ? BF16 : F16), (int64_t)r * p.ldc + c + e, v[e]);
         }
       }
+    };
+    if (Eb) {
+      typename VecIO<ET>::raw e0, e1;
+      bool h0 = fetch_e(tid, e0);
+#pragma unroll 1
+      for (int it = 0; it < ITR; it += 2) {
+        const int idx = tid + it * NT;
+        const bool h1 = fetch_e(idx + NT, e1);
+        row_vec(idx, &e0, h0);
+        if (it + 2 < ITR) h0 = fetch_e(idx + 2 * NT, e0);
+        row_vec(idx + NT, &e1, h1);
+      }
+    } else {
+#pragma unroll 1
+      for (int idx = tid; idx < SROWS * VPR; idx += NT) row_vec(idx, nullptr, false);
     }
     if (colpass) {
-      __syncthreads();
+      lds_barrier();
       for (int idx = tid; idx < BN * RVC; idx += NT) {
         const int ci = idx & 15, ri = (idx >> 4) & 3, blk = idx >> 6;
         const int cb = blk % (BN / 16), rb = blk / (BN / 16);
@@ -472,7 +523,7 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
         if (Ctb && c < p.ct_rows && r < p.ct_cols) VecIO<OT>::store(Ctb, (int64_t)c * p.ldct + r, v);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -481,10 +532,10 @@ __device__ inline void epilogue_fast(const GemmArgs& p, char* lds, f32x16 (&acc)
 // or transposed when the caller's matrix is m x n); bit 2 of flags[mat] marks a non-finite v.
 template <typename WT, class CFG>
 __device__ inline void epilogue_wupd(const GemmArgs& p, char* lds, f32x16 (&acc)[CFG::TM][CFG::TN],
-                                     int mat, int row0, int col0) {
-  constexpr int BN = CFG::BN, NT = CFG::NT, WTM = CFG::WTM, WTN = CFG::WTN, CP = CFG::CP;
-  constexpr int TM = CFG::TM, TN = CFG::TN, SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                     int mat, int row0, int col0, int lane) {
+  constexpr int BN = CFG::BN, NT = CFG::NT, WTM = CFG::WTM, CP = CFG::CP;
+  constexpr int SR = CFG::SR, SROWS = SR * WTM, VPR = BN / 8, RVC = SROWS / 8;
+  const int wave = wave_uniform(threadIdx.x >> 6), tid = wave * 64 + lane;
   const int wm = wave / CFG::WVN, wn = wave % CFG::WVN;
   float sc = 1.f;
   if (p.spow) {
@@ -495,60 +546,106 @@ __device__ inline void epilogue_wupd(const GemmArgs& p, char* lds, f32x16 (&acc)
   bool bad = false;
   float* Cs = reinterpret_cast<float*>(lds);
   // the same operations in the same order as the generic epilogue, so both give the same W
-  auto update = [&](int64_t wi, const float (&acc8)[8]) {
+  // (h: the vector lies inside W; its loaded value is always consumed, its store is not)
+  auto update = [&](int64_t wi, bool h, const typename VecIO<WT>::raw& wraw, const float (&acc8)[8]) {
     float w[8];
-    VecIO<WT>::load(Wb, wi, w);
+    VecIO<WT>::unpack(wraw, w);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = p.c2 * acc8[e];
       v *= sc;
-      bad |= !__builtin_isfinite(v);
+      bad |= h && !__builtin_isfinite(v);
       const float u = p.u_scale * v;
       w[e] = p.wd_mul * w[e] - p.lr * u;
     }
-    VecIO<WT>::store(Wb, wi, w);
+    if (h) VecIO<WT>::store(Wb, wi, w);
   };
   for (int sl = 0; sl < CFG::WVM / SR; ++sl) {
     const int srow0 = row0 + sl * SROWS;
     if (wm / SR == sl) {
-      const int lrow0 = (wm % SR) * WTM;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int r = lrow0 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            const int c = wn * WTN + j * 32 + (lane & 31);
-            Cs[r * CP + c] = acc[i][j][rr];
-          }
+      acc_to_slab<CFG>(Cs, acc, lane, wn, (wm % SR) * WTM);
     }
-    __syncthreads();
+    lds_barrier();
+    // each lane's 16-bit W vectors are loaded one vector ahead of their update, so that a load's
+    // wait does not also wait for the W stores issued in between (fp32 W: loaded at its use,
+    // which needs no extra registers)
+    constexpr bool PFW = sizeof(WT) == 2;
+    constexpr int ITR = SROWS * VPR / NT, ITC = BN * RVC / NT;
+    static_assert(ITR % 2 == 0 && ITR * NT == SROWS * VPR && ITC % 2 == 0 && ITC * NT == BN * RVC,
+                  "passes in pairs of iterations");
+    typename VecIO<WT>::raw w0, w1;
     if (!p.w_trans) {
-      for (int idx = tid; idx < SROWS * VPR; idx += NT) {
+      auto w_at = [&](int i, bool& h) {
+        const int r = srow0 + i / VPR, c = col0 + (i % VPR) * 8;
+        h = r < p.M && c < p.N;
+        return h ? (int64_t)r * p.ldw + c : (int64_t)0;
+      };
+      auto fetch_w = [&](int i, typename VecIO<WT>::raw& w) {
+        bool h;
+        const int64_t wi = w_at(i, h);
+        if (PFW) w = VecIO<WT>::load_raw(Wb, wi);
+        return h;
+      };
+      auto row_vec = [&](int idx, const typename VecIO<WT>::raw& w, bool) {
+        bool h;
+        const int64_t wi = w_at(idx, h);
         const int lr = idx / VPR, lc = (idx - lr * VPR) * 8;
-        const int r = srow0 + lr, c = col0 + lc;
-        if (r >= p.M || c >= p.N) continue;
         const float* cs = Cs + lr * CP + lc;
         const f32x4 a = *reinterpret_cast<const f32x4*>(cs), b = *reinterpret_cast<const f32x4*>(cs + 4);
         const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        update((int64_t)r * p.ldw + c, v);
+        update(wi, h, PFW ? w : VecIO<WT>::load_raw(Wb, wi), v);
+      };
+      bool h0 = fetch_w(tid, w0);
+#pragma unroll 1
+      for (int it = 0; it < ITR; it += 2) {
+        const int idx = tid + it * NT;
+        const bool h1 = fetch_w(idx + NT, w1);
+        row_vec(idx, w0, h0);
+        if (it + 2 < ITR) h0 = fetch_w(idx + 2 * NT, w0);
+        row_vec(idx + NT, w1, h1);
       }
     } else {
       // W is the caller's m x n matrix: column c of this n x m tile is row c of W
-      for (int idx = tid; idx < BN * RVC; idx += NT) {
-        const int ci = idx & 15, ri = (idx >> 4) & 3, blk = idx >> 6;
+      auto pos = [&](int i, int& lr, int& lc) {
+        const int ci = i & 15, ri = (i >> 4) & 3, blk = i >> 6;
         const int cb = blk % (BN / 16), rb = blk / (BN / 16);
-        const int lc = cb * 16 + ci, lr = (rb * 4 + ri) * 8;
+        lc = cb * 16 + ci;
+        lr = (rb * 4 + ri) * 8;
+      };
+      auto w_at = [&](int i, bool& h) {
+        int lr, lc;
+        pos(i, lr, lc);
         const int r = srow0 + lr, c = col0 + lc;
-        if (c >= p.N || r >= p.M) continue;
+        h = c < p.N && r < p.M;
+        return h ? (int64_t)c * p.ldw + r : (int64_t)0;
+      };
+      auto fetch_w = [&](int i, typename VecIO<WT>::raw& w) {
+        bool h;
+        const int64_t wi = w_at(i, h);
+        if (PFW) w = VecIO<WT>::load_raw(Wb, wi);
+        return h;
+      };
+      auto col_vec = [&](int idx, const typename VecIO<WT>::raw& w, bool) {
+        bool h;
+        const int64_t wi = w_at(idx, h);
+        int lr, lc;
+        pos(idx, lr, lc);
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = Cs[(lr + e) * CP + lc];
-        update((int64_t)c * p.ldw + r, v);
+        update(wi, h, PFW ? w : VecIO<WT>::load_raw(Wb, wi), v);
+      };
+      bool h0 = fetch_w(tid, w0);
+#pragma unroll 1
+      for (int it = 0; it < ITC; it += 2) {
+        const int idx = tid + it * NT;
+        const bool h1 = fetch_w(idx + NT, w1);
+        col_vec(idx, w0, h0);
+        if (it + 2 < ITC) h0 = fetch_w(idx + 2 * NT, w0);
+        col_vec(idx + NT, w1, h1);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (p.flags && __builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(p.flags + mat, 4);
 }
@@ -588,7 +685,8 @@ gemm_nt_kernel(const GemmBatch gb) {
   for (int g = 0; g < gb.ng; ++g)
     xtiles += xcd_part_lo(gb.g[g].nblocks, xcd + 1) - xcd_part_lo(gb.g[g].nblocks, xcd);
   for (int j = wgx; j < xtiles; j += per_xcd) {
-  // the lane's offsets are recomputed for every tile instead of being kept across tiles
+  // the lane's offsets (main loop and epilogue) are recomputed for every tile instead of being
+  // kept across tiles
   int lane_t = lane0;
   __asm__ __volatile__("" : "+v"(lane_t));
   const int lane = lane_t;
@@ -876,14 +974,14 @@ gemm_nt_kernel(const GemmBatch gb) {
 
   // ---------------------------------------------------------------- epilogue
   if constexpr (EPI != 0) {
-    if constexpr (EPI == 1) epilogue_fast<_Float16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 2) epilogue_fast<__bf16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 3) epilogue_fast<_Float16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 4) epilogue_fast<__bf16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 5) epilogue_fast<float, float, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0);
-    else if constexpr (EPI == 6) epilogue_wupd<__bf16, CFG>(p, lds, acc, mat, row0, col0);
-    else if constexpr (EPI == 7) epilogue_wupd<_Float16, CFG>(p, lds, acc, mat, row0, col0);
-    else epilogue_wupd<float, CFG>(p, lds, acc, mat, row0, col0);
+    if constexpr (EPI == 1) epilogue_fast<_Float16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0, lane);
+    else if constexpr (EPI == 2) epilogue_fast<__bf16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0, lane);
+    else if constexpr (EPI == 3) epilogue_fast<_Float16, __bf16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0, lane);
+    else if constexpr (EPI == 4) epilogue_fast<__bf16, _Float16, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0, lane);
+    else if constexpr (EPI == 5) epilogue_fast<float, float, TRI, CFG>(p, lds, acc, mat, ti, tj, row0, col0, lane);
+    else if constexpr (EPI == 6) epilogue_wupd<__bf16, CFG>(p, lds, acc, mat, row0, col0, lane);
+    else if constexpr (EPI == 7) epilogue_wupd<_Float16, CFG>(p, lds, acc, mat, row0, col0, lane);
+    else epilogue_wupd<float, CFG>(p, lds, acc, mat, row0, col0, lane);
     continue;
   } else {
   // A) finish v = s^spow (c2 acc + c1 E) + c0 [i == j] in registers
@@ -924,17 +1022,7 @@ gemm_nt_kernel(const GemmBatch gb) {
   const bool colpass = mirror || Ctb || (Wb && p.w_trans);
   for (int sl = 0; sl < CFG::WVM / SR; ++sl) {
     if (wm / SR == sl) {
-      const int lrow0 = (wm % SR) * WTM;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int r = lrow0 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            const int c = wn * WTN + j * 32 + (lane & 31);
-            Cs[r * CP + c] = acc[i][j][rr];
-          }
+      acc_to_slab<CFG>(Cs, acc, lane, wn, (wm % SR) * WTM);
     }
     __syncthreads();
     const int srow0 = row0 + sl * SROWS;
