@@ -64,47 +64,52 @@ def _lib():
         # pull in the system runtime and the process would hold two, and the library's one
         # would not see the device torch's tensors and streams live on.
         _torch()
-        lib = ctypes.CDLL(LIB_PATH)
-        P = ctypes.POINTER
-        vp, sz = ctypes.c_void_p, ctypes.c_size_t
-        lib.mns_workspace_bytes.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsNsParams),
-                                            ctypes.c_int64, P(sz)]
-        for fn in (lib.muon_ns_batched, lib.gram_ns_batched):
-            fn.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
-        lib.muon_step.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
-                                  P(MnsStepParams), P(MnsNsParams), vp, sz, vp, vp]
-        lib.muon_step_noalloc.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
-                                          P(MnsStepParams), P(MnsNsParams), vp, vp]
-        lib.gram_ns_trace.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
-        lib.mns_workspace_bytes_grouped.argtypes = [ctypes.c_int, ctypes.c_int, P(MnsTensor),
-                                                    P(MnsNsParams), P(sz)]
-        for fn in (lib.muon_ns_grouped, lib.gram_ns_grouped):
-            fn.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
-        lib.muon_step_grouped.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsTensor),
-                                          P(MnsTensor), P(MnsStepParams), P(MnsNsParams), vp, sz,
-                                          vp, vp]
-        pp = P(vp)
-        lib.adamw_step.argtypes = [ctypes.c_int, pp, pp, pp, pp, P(ctypes.c_int64), ctypes.c_int32,
-                                   P(MnsAdamwParams), vp]
-        lib.adamw_step.restype = ctypes.c_int
-        lib.mns_status_string.argtypes = [ctypes.c_int]
-        lib.mns_status_string.restype = ctypes.c_char_p
-        lib.mns_last_hip_error.argtypes = []
-        lib.mns_version.argtypes = []
-        lib.mns_timing_enable.argtypes = [ctypes.c_int]
-        lib.mns_timing_reset.argtypes = []
-        lib.mns_timing_query.argtypes = [ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]
-        lib.mns_timing_kinds.argtypes = []
-        lib.mns_kernel_kind_name.argtypes = [ctypes.c_int]
-        lib.mns_kernel_kind_name.restype = ctypes.c_char_p
-        for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched, lib.gram_ns_trace,
-                  lib.mns_workspace_bytes_grouped, lib.muon_ns_grouped, lib.gram_ns_grouped,
-                  lib.muon_step_grouped,
-                  lib.muon_step, lib.muon_step_noalloc, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
-                  lib.mns_timing_reset, lib.mns_timing_query, lib.mns_timing_kinds):
-            f.restype = ctypes.c_int
-        _LIB = lib
+        _LIB = declare(ctypes.CDLL(LIB_PATH))
     return _LIB
+
+
+def declare(lib):
+    """Set the argument and result types of every C function on a loaded copy of the library
+    (needs no GPU and does not import torch); returns the library."""
+    P = ctypes.POINTER
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.mns_workspace_bytes.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsNsParams),
+                                        ctypes.c_int64, P(sz)]
+    for fn in (lib.muon_ns_batched, lib.gram_ns_batched):
+        fn.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
+    lib.muon_step.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
+                              P(MnsStepParams), P(MnsNsParams), vp, sz, vp, vp]
+    lib.muon_step_noalloc.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsTensor), P(MnsTensor),
+                                      P(MnsStepParams), P(MnsNsParams), vp, vp]
+    lib.gram_ns_trace.argtypes = [P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
+    lib.mns_workspace_bytes_grouped.argtypes = [ctypes.c_int, ctypes.c_int, P(MnsTensor),
+                                                P(MnsNsParams), P(sz)]
+    for fn in (lib.muon_ns_grouped, lib.gram_ns_grouped):
+        fn.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsNsParams), vp, sz, vp, vp]
+    lib.muon_step_grouped.argtypes = [ctypes.c_int, P(MnsTensor), P(MnsTensor), P(MnsTensor),
+                                      P(MnsTensor), P(MnsStepParams), P(MnsNsParams), vp, sz,
+                                      vp, vp]
+    pp = P(vp)
+    lib.adamw_step.argtypes = [ctypes.c_int, pp, pp, pp, pp, P(ctypes.c_int64), ctypes.c_int32,
+                               P(MnsAdamwParams), vp]
+    lib.adamw_step.restype = ctypes.c_int
+    lib.mns_status_string.argtypes = [ctypes.c_int]
+    lib.mns_status_string.restype = ctypes.c_char_p
+    lib.mns_last_hip_error.argtypes = []
+    lib.mns_version.argtypes = []
+    lib.mns_timing_enable.argtypes = [ctypes.c_int]
+    lib.mns_timing_reset.argtypes = []
+    lib.mns_timing_query.argtypes = [ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]
+    lib.mns_timing_kinds.argtypes = []
+    lib.mns_kernel_kind_name.argtypes = [ctypes.c_int]
+    lib.mns_kernel_kind_name.restype = ctypes.c_char_p
+    for f in (lib.mns_workspace_bytes, lib.muon_ns_batched, lib.gram_ns_batched, lib.gram_ns_trace,
+              lib.mns_workspace_bytes_grouped, lib.muon_ns_grouped, lib.gram_ns_grouped,
+              lib.muon_step_grouped,
+              lib.muon_step, lib.muon_step_noalloc, lib.mns_last_hip_error, lib.mns_version, lib.mns_timing_enable,
+              lib.mns_timing_reset, lib.mns_timing_query, lib.mns_timing_kinds):
+        f.restype = ctypes.c_int
+    return lib
 
 
 def lib():
